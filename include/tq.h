@@ -1,0 +1,199 @@
+/*
+ * tq.h -- C ABI of the MI355X (gfx950) TurboQuant KV-cache codec.
+ *
+ * The codec stores, per vector x of dimension d, its L2 norm nu = |x|, and
+ * quantizes every coordinate of z = Pi (x / nu) with a scalar Lloyd-Max table
+ * for the Beta coordinate density; Pi u = H_d (D * u) / sqrt(d) is a
+ * randomized Walsh-Hadamard rotation (random sign flip D, then the Hadamard
+ * matrix).  TurboQuant_prod (keys) spends b-1 bits on that table and one bit
+ * per QJL row on the signs of S r, r = z - c[idx], S an m x d Gaussian
+ * matrix, so that inner products can be estimated without bias; it also
+ * stores gamma = |r|.  TurboQuant_mse (values) spends all b bits on the table.
+ *
+ * Sources (page titles and sections):
+ *  - "FibQuant: Quantizzazione Vettoriale Universale per la Compressione della
+ *    KV-Cache ad Accesso Casuale": "1. Enunciato del Problema" (fixed-rate
+ *    codes at fixed addresses; normalize, rotate, quantize), "2.3 Codifica e
+ *    Decodifica" (encoder and decoder steps), "5. Significato e Affermazioni"
+ *    (fixed addresses let decompression fuse into attention kernels).
+ *  - "Google presenta TurboQuant ..." (7minutos.es): "La mecánica geométrica
+ *    de TurboQuant" (Beta coordinate law, cost C(f_X, b), codebooks solved
+ *    once and stored), "Eliminación del sesgo interno del producto"
+ *    (TurboQuant_prod, 1-bit QJL on the residual, unbiased estimator).
+ *  - "Ablazione, Inferenza Statistica e Validazione per la Compressione della
+ *    KV-Cache": "Configurazione Sperimentale" (randomized Walsh-Hadamard
+ *    rotation, Beta Lloyd-Max codebook, QJL sketch on the key path only).
+ *  - "TurboESM: ...": "2. Metodologia" part A (RoPE first, then the rotation)
+ *    and part E (one fused pass: unpack, correct, attend with online softmax).
+ *
+ * Conventions for every entry point:
+ *  - Pointers documented as "device" point to GPU memory; "host" to CPU
+ *    memory.  The caller owns every buffer, the stream and the structs; the
+ *    library keeps no pointer after a call returns and allocates nothing.
+ *  - Calls that launch kernels enqueue them on `stream` and return at once;
+ *    they never synchronize the host.  A fault inside a kernel surfaces at the
+ *    caller's next synchronization, not as a status of the launching call.
+ *  - Arguments are validated on the host before anything is enqueued; an
+ *    invalid call enqueues nothing and returns a negative status.
+ *  - Vectors are rows of d elements, row-major, rows laid out
+ *    [batch][head][token] (token fastest).
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#ifndef TQ_STREAM_T_DEFINED
+#define TQ_STREAM_T_DEFINED
+typedef struct ihipStream_t* tq_stream_t; /* a hipStream_t; NULL = null stream */
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+enum {
+  TQ_OK = 0,
+  TQ_ERR_INVALID_ARG = -1,   /* null or inconsistent argument */
+  TQ_ERR_UNSUPPORTED = -2,   /* valid request this build has no kernel for */
+  TQ_ERR_NOT_CONVERGED = -3, /* codebook iteration hit its limit */
+  TQ_ERR_HIP = -4,           /* the HIP runtime reported a launch error */
+  TQ_ERR_WORKSPACE = -5      /* workspace null or smaller than required */
+};
+
+enum { TQ_MSE = 0, TQ_PROD = 1 };   /* codec mode */
+enum { TQ_F16 = 0, TQ_F32 = 1 };    /* element type of input vectors */
+
+#define TQ_MAX_LEVELS 16            /* 2^b' for b' <= 4 */
+#define TQ_MAX_D 1536
+
+/* Returns a static, human-readable name of a status code. */
+const char* tq_status_string(int status);
+
+/* ---- a0: codebook (host only) -----------------------------------------
+ * Lloyd-Max scalar quantizer for the density of one coordinate of a uniform
+ * point on S^{d-1}, f_d(x) ~ (1 - x^2)^((d-3)/2) on [-1, 1], at `bits`
+ * (1..4) bits: minimises the MSE cost C(f_X, b) of "La mecánica geométrica de
+ * TurboQuant", outer cells extending to -1 and +1.  Deterministic fp64.
+ *   centroids  host, 2^bits doubles, ascending (output)
+ *   thresholds host, 2^bits - 1 doubles, midpoints of neighbours (output)
+ * Returns TQ_OK, TQ_ERR_INVALID_ARG (d < 3, bits outside 1..4, null output)
+ * or TQ_ERR_NOT_CONVERGED.  Touches no GPU state; callable without a GPU. */
+int tq_build_codebook(int d, int bits, double* centroids, double* thresholds);
+
+/* ---- a1: one codec instance ---------------------------------------------
+ * Plain host struct; kernels receive the table and the sign mask by value.
+ * Fill it with tq_codec_init.  `code_bits` b' = bits - 1 for TQ_PROD and
+ * bits for TQ_MSE. */
+typedef struct tq_codec {
+  int32_t d;          /* 64, 128 or 1536 on the GPU */
+  int32_t mode;       /* TQ_MSE or TQ_PROD */
+  int32_t bits;       /* total bits per coordinate b */
+  int32_t code_bits;  /* scalar code width b' (1..4) */
+  int32_t m;          /* QJL rows: d for TQ_PROD, 0 for TQ_MSE */
+  int32_t reserved;
+  float centroids[TQ_MAX_LEVELS];   /* first 2^b' used, fp32 of the fp64 table */
+  float thresholds[TQ_MAX_LEVELS];  /* first 2^b' - 1 used */
+  uint32_t flip[TQ_MAX_D / 32];     /* bit i%32 of word i/32 set <=> D_i = -1 */
+  const float* S;     /* device, m x d row-major fp32, p_i = sum_k S[i][k] r_k;
+                         NULL for TQ_MSE */
+} tq_codec;
+
+/* Builds the table for (d, b') with tq_build_codebook, rounds it to fp32 and
+ * fills `codec`.  flip: host, ceil(d/32) words in the layout above.  S: the
+ * caller's device matrix for TQ_PROD (m = d rows), ignored for TQ_MSE.
+ * Host only.  Returns TQ_OK or TQ_ERR_INVALID_ARG / TQ_ERR_NOT_CONVERGED. */
+int tq_codec_init(tq_codec* codec, int d, int mode, int bits,
+                  const uint32_t* flip, const float* S);
+
+/* ---- a7: packed planes ----------------------------------------------------
+ * Fixed rate and fixed addresses: row j's codes start at byte j*(d*b'/8) of
+ * `idx` and form one LSB-first bit stream (code i in stream bits
+ * [i*b', (i+1)*b'), stream bit k = bit k%8 of byte k/8); its QJL bits start at
+ * byte j*(m/8) of `qjl`, bit i = 1 iff (S r)_i >= 0, same bit order.  All
+ * device pointers; idx and qjl 16-byte aligned. */
+typedef struct tq_packed {
+  uint8_t* idx;   /* n rows of d*b'/8 bytes */
+  uint8_t* qjl;   /* n rows of m/8 bytes (TQ_PROD), else NULL */
+  float* norm;    /* n floats: nu = |x| */
+  float* rnorm;   /* n floats: gamma = |r| (TQ_PROD), else NULL */
+} tq_packed;
+
+/* RoPE before the rotation ("TurboESM", "2. Metodologia" part A): interleaved
+ * pairs (2i, 2i+1) rotated by position * base^(-2i/d).  Row r of an encode
+ * call sits at position r % seq_len; query a of an attend call at position
+ * pos0 + a. */
+typedef struct tq_rope {
+  float base;       /* e.g. 10000 */
+  int32_t pos0;     /* first query position (attend only) */
+  int64_t seq_len;  /* tokens per sequence (encode only) */
+} tq_rope;
+
+/* ---- a2..a7: encode --------------------------------------------------------
+ * Encodes n_rows rows of K with `kc` into `kout` and n_rows rows of V with
+ * `vc` into `vout` in one launch; pass NULL for a side to skip it.  Per row:
+ * (RoPE on K if `rope` is not NULL), nu = |x|, z = Pi x / nu, idx_i =
+ * #{k : z_i >= t_k}, and for TQ_PROD r = z - c[idx], gamma = |r|, signs of
+ * S r ("FibQuant" 2.3; "Google presenta TurboQuant" mechanics and prod
+ * sections).  The zero vector encodes as z = 0 with nu = 0.
+ *   k, v      device, n_rows x d elements of type `dtype`, 16-byte aligned
+ *   kc, vc    host structs (kc TQ_PROD or TQ_MSE; vc either)
+ *   kout/vout host structs of device planes sized for n_rows
+ * Returns TQ_OK, TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED or TQ_ERR_HIP. */
+int tq_encode_kv(const tq_codec* kc, const tq_codec* vc, const void* k,
+                 const void* v, int dtype, int64_t n_rows, const tq_rope* rope,
+                 const tq_packed* kout, const tq_packed* vout,
+                 tq_stream_t stream);
+
+/* ---- a8..a11: attention from codes ----------------------------------------
+ * For every batch b, query head h (KV head g = h / (hq / hkv)) and query a:
+ *   s_j = scale * nu_j * ( <q', c_K[idx_j]> + sqrt(pi/2)/m * gamma_j *
+ *                          <S q', 2 sigma_j - 1> ),   q' = Pi RoPE(q)
+ *   o   = Pi_V^T ( sum_j softmax(s)_j * nu^V_j * c_V[idx^V_j] )
+ * over all ctx tokens (no causal mask), computed in one pass over the codes
+ * with an online softmax split over token ranges and merged by log-sum-exp
+ * ("TurboESM" 2E; "Google presenta TurboQuant", unbiased estimator).
+ *   kc  TQ_PROD codec of the keys; vc TQ_MSE codec of the values
+ *   q   device [batch][hq][n_q][d] of `q_dtype`
+ *   k,v host structs of device planes, rows [batch][hkv][ctx]
+ *   scale  0 selects 1/sqrt(d)
+ *   out device [batch][hq][n_q][d] fp32
+ *   scores_out  NULL, or device [batch][hq][n_q][ctx] fp32 receiving s_j
+ *   workspace   device, >= tq_attend_decode_workspace(...) bytes, zero-filled
+ *               before its first use; each call leaves it ready for the next.
+ * Calls that share one workspace must not overlap in time. */
+size_t tq_attend_decode_workspace(int batch, int n_q, int hq, int hkv,
+                                  int64_t ctx, int d);
+int tq_attend_decode(const tq_codec* kc, const tq_codec* vc, const void* q,
+                     int q_dtype, int batch, int n_q, int hq, int hkv,
+                     const tq_rope* q_rope, const tq_packed* k,
+                     const tq_packed* v, int64_t ctx, float scale, float* out,
+                     float* scores_out, void* workspace,
+                     size_t workspace_bytes, tq_stream_t stream);
+
+/* ---- a12: inner-product scan (+ top-k) --------------------------------------
+ * est(a, j) = nu_j ( <Pi q_a, c[idx_j]> + sqrt(pi/2)/m gamma_j
+ *                    <S Pi q_a, 2 sigma_j - 1> )  (mse: first term only)
+ * for n_q queries against n packed rows ("Google presenta TurboQuant",
+ * "Velocidad y eficiencia de indexación").
+ *   q        device [n_q][d] of `q_dtype`
+ *   out      NULL, or device [n_q][n] fp32
+ *   top_k    0, or 1..64: per query the top_k largest estimates, descending,
+ *            ties to the lower row index, into top_ids [n_q][top_k] (int64)
+ *            and top_scores [n_q][top_k] (fp32), device
+ *   workspace device, >= tq_inner_product_workspace(...) bytes (may be NULL
+ *            when that is 0). */
+size_t tq_inner_product_workspace(int64_t n_q, int64_t n, int d, int top_k);
+int tq_inner_product(const tq_codec* c, const void* q, int q_dtype,
+                     int64_t n_q, const tq_packed* x, int64_t n, float* out,
+                     int top_k, int64_t* top_ids, float* top_scores,
+                     void* workspace, size_t workspace_bytes,
+                     tq_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H */

@@ -1,0 +1,284 @@
+"""Python binding of the gfx950 TurboQuant KV-cache codec library (libtq.so).
+
+Argument marshalling only: every step of encode, attention and search runs
+in the HIP kernels behind the C ABI declared in include/tq.h.  PyTorch
+provides device memory and the current stream; nothing here computes.
+
+The library must be built (``python -m kv_cache_vector_04_amd.build``);
+importing this module fails loudly when it is missing.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+import torch  # loaded first so libtq.so binds to the HIP runtime torch uses
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtq.so")
+
+TQ_OK, TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED = 0, -1, -2
+TQ_ERR_NOT_CONVERGED, TQ_ERR_HIP, TQ_ERR_WORKSPACE = -3, -4, -5
+TQ_MSE, TQ_PROD = 0, 1
+TQ_F16, TQ_F32 = 0, 1
+
+EXPORTS = ("tq_status_string", "tq_build_codebook", "tq_codec_init", "tq_encode_kv",
+           "tq_attend_decode_workspace", "tq_attend_decode",
+           "tq_inner_product_workspace", "tq_inner_product")
+
+
+class TQError(RuntimeError):
+    def __init__(self, status, what):
+        super().__init__("%s failed: %s (%d)" % (what, status_string(status), status))
+        self.status = status
+
+
+class TQCodec(ctypes.Structure):
+    _fields_ = [("d", ctypes.c_int32), ("mode", ctypes.c_int32), ("bits", ctypes.c_int32),
+                ("code_bits", ctypes.c_int32), ("m", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("centroids", ctypes.c_float * 16), ("thresholds", ctypes.c_float * 16),
+                ("flip", ctypes.c_uint32 * 48), ("S", ctypes.c_void_p)]
+
+
+class TQPacked(ctypes.Structure):
+    _fields_ = [("idx", ctypes.c_void_p), ("qjl", ctypes.c_void_p),
+                ("norm", ctypes.c_void_p), ("rnorm", ctypes.c_void_p)]
+
+
+class TQRope(ctypes.Structure):
+    _fields_ = [("base", ctypes.c_float), ("pos0", ctypes.c_int32), ("seq_len", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libtq.so (raises ImportError if it was not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libtq.so is not built: run `python -m kv_cache_vector_04_amd.build` "
+                          "(or __graft_entry__.build()) first; there is no fallback path")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I, I64, SZ, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+    L.tq_status_string.restype = ctypes.c_char_p
+    L.tq_status_string.argtypes = [I]
+    L.tq_build_codebook.restype = I
+    L.tq_build_codebook.argtypes = [I, I, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
+    L.tq_codec_init.restype = I
+    L.tq_codec_init.argtypes = [ctypes.POINTER(TQCodec), I, I, I, ctypes.POINTER(ctypes.c_uint32), P]
+    L.tq_encode_kv.restype = I
+    L.tq_encode_kv.argtypes = [ctypes.POINTER(TQCodec), ctypes.POINTER(TQCodec), P, P, I, I64,
+                               ctypes.POINTER(TQRope), ctypes.POINTER(TQPacked),
+                               ctypes.POINTER(TQPacked), P]
+    L.tq_attend_decode_workspace.restype = SZ
+    L.tq_attend_decode_workspace.argtypes = [I, I, I, I, I64, I]
+    L.tq_attend_decode.restype = I
+    L.tq_attend_decode.argtypes = [ctypes.POINTER(TQCodec), ctypes.POINTER(TQCodec), P, I, I, I, I, I,
+                                   ctypes.POINTER(TQRope), ctypes.POINTER(TQPacked),
+                                   ctypes.POINTER(TQPacked), I64, F, P, P, P, SZ, P]
+    L.tq_inner_product_workspace.restype = SZ
+    L.tq_inner_product_workspace.argtypes = [I64, I64, I, I]
+    L.tq_inner_product.restype = I
+    L.tq_inner_product.argtypes = [ctypes.POINTER(TQCodec), P, I, I64, ctypes.POINTER(TQPacked), I64,
+                                   P, I, P, P, P, SZ, P]
+    _lib = L
+    return L
+
+
+def status_string(status):
+    return lib().tq_status_string(int(status)).decode()
+
+
+def _check(status, what):
+    if status != TQ_OK:
+        raise TQError(status, what)
+
+
+def build_codebook(d, bits):
+    """Host Lloyd-Max table of the library: (centroids, thresholds) fp64."""
+    n = 1 << bits
+    c = (ctypes.c_double * n)()
+    t = (ctypes.c_double * max(n - 1, 1))()
+    _check(lib().tq_build_codebook(int(d), int(bits), c, t), "tq_build_codebook")
+    return np.array(c[:], dtype=np.float64), np.array(t[:n - 1], dtype=np.float64)
+
+
+def flip_words(flip):
+    """bool sign-flip vector (True = -1) -> uint32 words, bit i%32 of word i/32."""
+    flip = np.asarray(flip, dtype=bool)
+    d = flip.shape[0]
+    bits = np.zeros(((d + 31) // 32) * 32, dtype=np.uint8)
+    bits[:d] = flip
+    return np.packbits(bits.reshape(-1, 32), axis=1, bitorder="little").view(np.uint32).ravel()
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float16:
+        return TQ_F16
+    if t.dtype == torch.float32:
+        return TQ_F32
+    raise TypeError("vectors must be float16 or float32, got %s" % t.dtype)
+
+
+def _device_tensor(t, name):
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError("%s must be a CUDA (HIP) tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+class Codec:
+    """One codec instance: dimension, mode, total bits, sign flip D and (prod)
+    the QJL matrix S, held on the device."""
+
+    def __init__(self, d, mode, bits, flip, S=None, device="cuda"):
+        self.d, self.mode, self.bits = int(d), int(mode), int(bits)
+        self.flip = np.asarray(flip, dtype=bool)
+        self.S = None
+        if mode == TQ_PROD:
+            S = torch.as_tensor(S, dtype=torch.float32)
+            self.S = S.to(device).contiguous() if S.device.type != "cuda" else S.contiguous()
+        self.struct = TQCodec()
+        words = flip_words(self.flip)
+        wbuf = (ctypes.c_uint32 * len(words))(*[int(w) for w in words])
+        _check(lib().tq_codec_init(ctypes.byref(self.struct), self.d, self.mode, self.bits, wbuf,
+                                   _ptr(self.S)), "tq_codec_init")
+
+    @property
+    def code_bits(self):
+        return self.struct.code_bits
+
+    @property
+    def m(self):
+        return self.struct.m
+
+    def centroids(self):
+        return np.array(self.struct.centroids[:1 << self.code_bits], dtype=np.float32)
+
+    def thresholds(self):
+        return np.array(self.struct.thresholds[:(1 << self.code_bits) - 1], dtype=np.float32)
+
+
+class Packed:
+    """Packed planes of n vectors (device tensors)."""
+
+    def __init__(self, codec, n, device="cuda"):
+        self.n = int(n)
+        row = codec.d * codec.code_bits // 8
+        self.idx = torch.empty((self.n, row), dtype=torch.uint8, device=device)
+        self.norm = torch.empty((self.n,), dtype=torch.float32, device=device)
+        if codec.mode == TQ_PROD:
+            self.qjl = torch.empty((self.n, codec.m // 8), dtype=torch.uint8, device=device)
+            self.rnorm = torch.empty((self.n,), dtype=torch.float32, device=device)
+        else:
+            self.qjl = None
+            self.rnorm = None
+        self.struct = TQPacked(_ptr(self.idx).value, _ptr(self.qjl).value, _ptr(self.norm).value,
+                               _ptr(self.rnorm).value)
+
+
+def encode_kv(kcodec, vcodec, k, v, rope=None, kout=None, vout=None, stream=None):
+    """Encode rows of k with kcodec and rows of v with vcodec (either side may
+    be None).  k / v: device tensors [..., d], fp16 or fp32.  rope: None or
+    (base, seq_len), applied to k.  Returns (kout, vout) Packed."""
+    n = None
+    dt = None
+    for c, x in ((kcodec, k), (vcodec, v)):
+        if c is None:
+            continue
+        _device_tensor(x, "input")
+        if x.shape[-1] != c.d:
+            raise ValueError("last dimension must be d=%d" % c.d)
+        rows = x.numel() // c.d
+        n = rows if n is None else n
+        if rows != n:
+            raise ValueError("k and v must hold the same number of rows")
+        d2 = _dtype_code(x)
+        dt = d2 if dt is None else dt
+        if d2 != dt:
+            raise ValueError("k and v must share a dtype")
+    dev = (k if kcodec is not None else v).device
+    if kcodec is not None and kout is None:
+        kout = Packed(kcodec, n, dev)
+    if vcodec is not None and vout is None:
+        vout = Packed(vcodec, n, dev)
+    r = None
+    if rope is not None:
+        r = TQRope(float(rope[0]), 0, int(rope[1]))
+    st = lib().tq_encode_kv(ctypes.byref(kcodec.struct) if kcodec else None,
+                            ctypes.byref(vcodec.struct) if vcodec else None,
+                            _ptr(k) if kcodec else None, _ptr(v) if vcodec else None, dt, n,
+                            ctypes.byref(r) if r is not None else None,
+                            ctypes.byref(kout.struct) if kcodec else None,
+                            ctypes.byref(vout.struct) if vcodec else None, _stream(stream))
+    _check(st, "tq_encode_kv")
+    return kout, vout
+
+
+def attend_workspace_bytes(batch, n_q, hq, hkv, ctx, d):
+    return int(lib().tq_attend_decode_workspace(batch, n_q, hq, hkv, ctx, d))
+
+
+def attend_decode(kcodec, vcodec, q, kpk, vpk, ctx, hkv, scale=0.0, rope=None, out=None,
+                  want_scores=False, workspace=None, stream=None):
+    """Attention from codes.  q: device [batch, hq, n_q, d] fp16/fp32; kpk,
+    vpk: Packed rows [batch][hkv][ctx].  rope: None or (base, pos0).
+    Returns out [batch, hq, n_q, d] fp32 (and scores [batch, hq, n_q, ctx])."""
+    _device_tensor(q, "q")
+    batch, hq, n_q, d = q.shape
+    if out is None:
+        out = torch.empty((batch, hq, n_q, d), dtype=torch.float32, device=q.device)
+    scores = None
+    if want_scores:
+        scores = torch.empty((batch, hq, n_q, ctx), dtype=torch.float32, device=q.device)
+    need = attend_workspace_bytes(batch, n_q, hq, hkv, ctx, d)
+    if workspace is None:
+        workspace = torch.zeros((max(need, 16),), dtype=torch.uint8, device=q.device)
+    r = TQRope(float(rope[0]), int(rope[1]), 0) if rope is not None else None
+    st = lib().tq_attend_decode(ctypes.byref(kcodec.struct), ctypes.byref(vcodec.struct), _ptr(q),
+                                _dtype_code(q), batch, n_q, hq, hkv,
+                                ctypes.byref(r) if r is not None else None,
+                                ctypes.byref(kpk.struct), ctypes.byref(vpk.struct), int(ctx),
+                                float(scale), _ptr(out), _ptr(scores), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "tq_attend_decode")
+    return (out, scores) if want_scores else out
+
+
+def inner_product_workspace_bytes(n_q, n, d, top_k):
+    return int(lib().tq_inner_product_workspace(n_q, n, d, top_k))
+
+
+def inner_product(codec, q, pk, n, top_k=0, want_matrix=True, workspace=None, stream=None):
+    """Estimated inner products of q [n_q, d] against n packed rows.  Returns
+    the [n_q, n] matrix (if want_matrix) and, for top_k > 0, (ids, scores)."""
+    _device_tensor(q, "q")
+    n_q, d = q.shape
+    out = torch.empty((n_q, n), dtype=torch.float32, device=q.device) if want_matrix else None
+    ids = vals = None
+    if top_k:
+        ids = torch.empty((n_q, top_k), dtype=torch.int64, device=q.device)
+        vals = torch.empty((n_q, top_k), dtype=torch.float32, device=q.device)
+    need = inner_product_workspace_bytes(n_q, n, d, top_k)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
+    st = lib().tq_inner_product(ctypes.byref(codec.struct), _ptr(q), _dtype_code(q), n_q,
+                                ctypes.byref(pk.struct), int(n), _ptr(out), int(top_k), _ptr(ids),
+                                _ptr(vals), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "tq_inner_product")
+    if top_k:
+        return out, ids, vals
+    return out

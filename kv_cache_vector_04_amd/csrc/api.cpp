@@ -1,0 +1,157 @@
+// C-ABI entry points: argument validation on the host, then the launchers.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "internal.hpp"
+#include "tq.h"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool gpu_dim(int d) { return d == 64 || d == 128; }
+
+int check_codec(const tq_codec* c) {
+  if (c == nullptr) return TQ_ERR_INVALID_ARG;
+  if (c->mode != TQ_MSE && c->mode != TQ_PROD) return TQ_ERR_INVALID_ARG;
+  if (c->code_bits < 1 || c->code_bits > 4) return TQ_ERR_INVALID_ARG;
+  if (c->bits != c->code_bits + (c->mode == TQ_PROD ? 1 : 0)) return TQ_ERR_INVALID_ARG;
+  if (c->mode == TQ_PROD && (c->m != c->d || c->S == nullptr || !aligned(c->S, 16)))
+    return TQ_ERR_INVALID_ARG;
+  if (c->mode == TQ_MSE && c->m != 0) return TQ_ERR_INVALID_ARG;
+  if (!gpu_dim(c->d)) return TQ_ERR_UNSUPPORTED;
+  return TQ_OK;
+}
+
+int check_planes(const tq_codec* c, const tq_packed* p) {
+  if (p == nullptr || p->idx == nullptr || p->norm == nullptr) return TQ_ERR_INVALID_ARG;
+  const size_t row_bytes = (size_t)c->d * c->code_bits / 8;
+  if (!aligned(p->idx, row_bytes % 16 == 0 ? 16 : 8) || !aligned(p->norm, 4))
+    return TQ_ERR_INVALID_ARG;
+  if (c->mode == TQ_PROD) {
+    if (p->qjl == nullptr || p->rnorm == nullptr) return TQ_ERR_INVALID_ARG;
+    if (!aligned(p->qjl, 8) || !aligned(p->rnorm, 4)) return TQ_ERR_INVALID_ARG;
+  }
+  return TQ_OK;
+}
+
+tqk::RopeHost rope_of(const tq_rope* r) {
+  tqk::RopeHost h = {};
+  if (r != nullptr) {
+    h.on = true;
+    h.base = r->base;
+    h.pos0 = r->pos0;
+    h.seq_len = r->seq_len;
+  }
+  return h;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_ERR_HIP; }
+
+}  // namespace
+
+namespace tqk {
+int device_cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
+}
+}  // namespace tqk
+
+extern "C" int tq_encode_kv(const tq_codec* kc, const tq_codec* vc, const void* k,
+                            const void* v, int dtype, int64_t n_rows, const tq_rope* rope,
+                            const tq_packed* kout, const tq_packed* vout,
+                            tq_stream_t stream) {
+  if (kc == nullptr && vc == nullptr) return TQ_ERR_INVALID_ARG;
+  if (n_rows < 0) return TQ_ERR_INVALID_ARG;
+  if (dtype != TQ_F16 && dtype != TQ_F32) return TQ_ERR_INVALID_ARG;
+  if (rope != nullptr) {
+    if (kc == nullptr || !(rope->base > 0.f) || rope->seq_len <= 0) return TQ_ERR_INVALID_ARG;
+    // RoPE is fused for the d = 64 fp16 key path (the RoPE workload here)
+    if (dtype != TQ_F16 || kc->d != 64) return TQ_ERR_UNSUPPORTED;
+  }
+  const tq_codec* cs[2] = {kc, vc};
+  const void* xs[2] = {k, v};
+  const tq_packed* outs[2] = {kout, vout};
+  for (int s = 0; s < 2; ++s) {
+    if (cs[s] == nullptr) continue;
+    int st = check_codec(cs[s]);
+    if (st != TQ_OK) return st;
+    if ((st = check_planes(cs[s], outs[s])) != TQ_OK) return st;
+    if (xs[s] == nullptr || !aligned(xs[s], 16)) return TQ_ERR_INVALID_ARG;
+  }
+  if (n_rows == 0) return TQ_OK;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  for (int s = 0; s < 2; ++s) {
+    if (cs[s] == nullptr) continue;
+    const tqk::RopeHost rh = s == 0 ? rope_of(rope) : tqk::RopeHost{};
+    const int st = hip_status(tqk::launch_encode(*cs[s], xs[s], dtype, n_rows, rh, *outs[s], hs));
+    if (st != TQ_OK) return st;
+  }
+  return TQ_OK;
+}
+
+extern "C" size_t tq_attend_decode_workspace(int batch, int n_q, int hq, int hkv,
+                                             int64_t ctx, int d) {
+  if (batch <= 0 || n_q <= 0 || hq <= 0 || hkv <= 0 || ctx <= 0 || d <= 0) return 0;
+  return tqk::attend_workspace_bytes(batch, n_q, hq, hkv, ctx, d);
+}
+
+extern "C" int tq_attend_decode(const tq_codec* kc, const tq_codec* vc, const void* q,
+                                int q_dtype, int batch, int n_q, int hq, int hkv,
+                                const tq_rope* q_rope, const tq_packed* k,
+                                const tq_packed* v, int64_t ctx, float scale, float* out,
+                                float* scores_out, void* workspace, size_t workspace_bytes,
+                                tq_stream_t stream) {
+  int st = check_codec(kc);
+  if (st != TQ_OK) return st;
+  if ((st = check_codec(vc)) != TQ_OK) return st;
+  if (kc->mode != TQ_PROD || vc->mode != TQ_MSE) return TQ_ERR_UNSUPPORTED;
+  if (kc->d != vc->d) return TQ_ERR_INVALID_ARG;
+  if (q == nullptr || out == nullptr || !aligned(q, 16) || !aligned(out, 16))
+    return TQ_ERR_INVALID_ARG;
+  if (q_dtype != TQ_F16 && q_dtype != TQ_F32) return TQ_ERR_INVALID_ARG;
+  if (batch <= 0 || n_q <= 0 || hq <= 0 || hkv <= 0 || ctx <= 0) return TQ_ERR_INVALID_ARG;
+  if (hq % hkv) return TQ_ERR_INVALID_ARG;
+  if (hq / hkv > 16) return TQ_ERR_UNSUPPORTED;
+  if (!(scale >= 0.f)) return TQ_ERR_INVALID_ARG;
+  if (q_rope != nullptr && (!(q_rope->base > 0.f) || q_rope->pos0 < 0)) return TQ_ERR_INVALID_ARG;
+  if ((st = check_planes(kc, k)) != TQ_OK) return st;
+  if ((st = check_planes(vc, v)) != TQ_OK) return st;
+  const size_t need = tqk::attend_workspace_bytes(batch, n_q, hq, hkv, ctx, kc->d);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16)))
+    return TQ_ERR_WORKSPACE;
+  return hip_status(tqk::launch_attend(*kc, *vc, q, q_dtype, batch, n_q, hq, hkv,
+                                       rope_of(q_rope), *k, *v, ctx, scale, out, scores_out,
+                                       workspace, reinterpret_cast<hipStream_t>(stream)));
+}
+
+extern "C" size_t tq_inner_product_workspace(int64_t n_q, int64_t n, int d, int top_k) {
+  if (n_q <= 0 || n <= 0 || d <= 0 || top_k < 0) return 0;
+  return tqk::scan_workspace_bytes(n_q, n, d, top_k);
+}
+
+extern "C" int tq_inner_product(const tq_codec* c, const void* q, int q_dtype, int64_t n_q,
+                                const tq_packed* x, int64_t n, float* out, int top_k,
+                                int64_t* top_ids, float* top_scores, void* workspace,
+                                size_t workspace_bytes, tq_stream_t stream) {
+  int st = check_codec(c);
+  if (st != TQ_OK) return st;
+  if (q == nullptr || !aligned(q, 16)) return TQ_ERR_INVALID_ARG;
+  if (q_dtype != TQ_F16 && q_dtype != TQ_F32) return TQ_ERR_INVALID_ARG;
+  if (n_q <= 0 || n <= 0) return TQ_ERR_INVALID_ARG;
+  if (top_k < 0 || top_k > 64) return TQ_ERR_INVALID_ARG;
+  if (top_k > 0 && (top_ids == nullptr || top_scores == nullptr)) return TQ_ERR_INVALID_ARG;
+  if (top_k == 0 && out == nullptr) return TQ_ERR_INVALID_ARG;
+  if (top_k > n) return TQ_ERR_INVALID_ARG;
+  if ((st = check_planes(c, x)) != TQ_OK) return st;
+  const size_t need = tqk::scan_workspace_bytes(n_q, n, c->d, top_k);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16)))
+    return TQ_ERR_WORKSPACE;
+  return hip_status(tqk::launch_scan(*c, q, q_dtype, n_q, *x, n, out, top_k, top_ids, top_scores,
+                                     workspace, reinterpret_cast<hipStream_t>(stream)));
+}

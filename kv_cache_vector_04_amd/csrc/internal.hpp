@@ -1,0 +1,40 @@
+// Launchers behind the C ABI (host side).  Arguments are validated by the
+// entry points in api.cpp before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tq.h"
+
+namespace tqk {
+
+struct RopeHost {
+  bool on;
+  float base;
+  int32_t pos0;
+  int64_t seq_len;
+};
+
+// Encode n_rows rows of one tensor with one codec.
+hipError_t launch_encode(const tq_codec& c, const void* x, int dtype,
+                         int64_t n_rows, const RopeHost& rope,
+                         const tq_packed& out, hipStream_t stream);
+
+size_t attend_workspace_bytes(int batch, int n_q, int hq, int hkv, int64_t ctx, int d);
+hipError_t launch_attend(const tq_codec& kc, const tq_codec& vc, const void* q,
+                         int q_dtype, int batch, int n_q, int hq, int hkv,
+                         const RopeHost& rope, const tq_packed& k,
+                         const tq_packed& v, int64_t ctx, float scale,
+                         float* out, float* scores_out, void* workspace,
+                         hipStream_t stream);
+
+size_t scan_workspace_bytes(int64_t n_q, int64_t n, int d, int top_k);
+hipError_t launch_scan(const tq_codec& c, const void* q, int q_dtype,
+                       int64_t n_q, const tq_packed& x, int64_t n, float* out,
+                       int top_k, int64_t* top_ids, float* top_scores,
+                       void* workspace, hipStream_t stream);
+
+int device_cu_count();
+
+}  // namespace tqk

@@ -94,6 +94,10 @@ def lloyd_max(d, bits, tol=1e-15, max_iter=200000):
         step = np.max(np.abs(c_new - c))
         c = c_new
         if step <= tol:
+            # f_d is even, so the optimum is symmetric (c_k = -c_{N-1-k});
+            # symmetrising removes the rounding noise, which puts the middle
+            # threshold exactly at 0.
+            c = 0.5 * (c - c[::-1])
             return c, _thresholds(c), it
     raise RuntimeError("Lloyd-Max did not converge (d=%d, bits=%d)" % (d, bits))
 

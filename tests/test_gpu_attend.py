@@ -1,0 +1,119 @@
+"""GPU attention-from-codes parity (tq_attend_decode)."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from parity import check_rows, gpu_codes, to_np
+
+pytestmark = pytest.mark.gpu
+
+tq = pytest.importorskip("kv_cache_vector_04_amd")
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _codes_4d(pk, codec, B, Hkv, ctx):
+    g = gpu_codes(pk, codec.d, codec.code_bits, codec.m if codec.mode == tq.TQ_PROD else None)
+    return {k: v.reshape((B, Hkv, ctx) + v.shape[1:]) for k, v in g.items()}
+
+
+def _oracle_attention(q, kpk, vpk, kc, vc, draws, B, Hkv, ctx, q_rope_pos=None):
+    d = kc.d
+    kcent, _ = oracle.codebook(d, kc.code_bits)
+    vcent, _ = oracle.codebook(d, vc.code_bits)
+    kb = {"signs": draws.flip, "centroids": kcent, "S": draws.S.astype(np.float64)}
+    vb = {"signs": draws.flip, "centroids": vcent}
+    q64 = q.astype(np.float64)
+    if q_rope_pos is not None:
+        q64 = oracle.rope_interleaved(q64, q_rope_pos)
+    return oracle.attention_from_codes(q64, _codes_4d(kpk, kc, B, Hkv, ctx),
+                                       _codes_4d(vpk, vc, B, Hkv, ctx), kb, vb, return_scores=True)
+
+
+def _run(B, Hq, Hkv, ctx, nq, d, kbits, vbits, seed, dist="normal"):
+    rng = np.random.default_rng(seed)
+    if dist == "t":
+        k = rng.standard_t(3, (B, Hkv, ctx, d)).astype(np.float16)
+        v = rng.standard_t(3, (B, Hkv, ctx, d)).astype(np.float16)
+    else:
+        k = rng.standard_normal((B, Hkv, ctx, d)).astype(np.float16)
+        v = rng.standard_normal((B, Hkv, ctx, d)).astype(np.float16)
+    q = rng.standard_normal((B, Hq, nq, d)).astype(np.float16)
+    draws = synth.codec_draws(rng, d, m=d)
+    kc = tq.Codec(d, tq.TQ_PROD, kbits, draws.flip, draws.S)
+    vc = tq.Codec(d, tq.TQ_MSE, vbits, draws.flip)
+    kpk, vpk = tq.encode_kv(kc, vc, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda())
+    out, sc = tq.attend_decode(kc, vc, torch.from_numpy(q).cuda(), kpk, vpk, ctx, Hkv, want_scores=True)
+    torch.cuda.synchronize()
+    ref_out, ref_sc = _oracle_attention(q, kpk, vpk, kc, vc, draws, B, Hkv, ctx)
+    e1 = check_rows(to_np(sc), ref_sc)
+    e2 = check_rows(to_np(out), ref_out)
+    return e1, e2
+
+
+def test_attend_gqa_decode_full():
+    say("attend gqa-decode: 32 q heads, 8 kv heads, ctx 32768, d 128, K prod b=4, V mse b=4")
+    w = synth.gqa_decode()
+    kc = tq.Codec(128, tq.TQ_PROD, 4, w["codec"].flip, w["codec"].S)
+    vc = tq.Codec(128, tq.TQ_MSE, 4, w["codec"].flip)
+    kpk, vpk = tq.encode_kv(kc, vc, torch.from_numpy(w["k"]).cuda(), torch.from_numpy(w["v"]).cuda())
+    q = w["q"].reshape(1, 32, 1, 128)
+    out, sc = tq.attend_decode(kc, vc, torch.from_numpy(q).cuda(), kpk, vpk, 32768, 8, want_scores=True)
+    torch.cuda.synchronize()
+    ref_out, ref_sc = _oracle_attention(q, kpk, vpk, kc, vc, w["codec"], 1, 8, 32768)
+    print("scores max row rel err", check_rows(to_np(sc), ref_sc),
+          "| out max row rel err", check_rows(to_np(out), ref_out))
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,ctx,nq,d,kb,vb", [
+    (1, 4, 4, 1, 1, 128, 4, 4),
+    (1, 8, 2, 257, 1, 128, 3, 3),
+    (2, 6, 3, 1000, 3, 128, 4, 4),
+    (1, 16, 1, 4099, 2, 128, 3, 4),
+    (1, 4, 2, 700, 5, 64, 3, 3),
+    (2, 2, 2, 300, 17, 64, 2, 2),
+])
+def test_attend_shapes(B, Hq, Hkv, ctx, nq, d, kb, vb):
+    say("attend B=%d Hq=%d Hkv=%d ctx=%d nq=%d d=%d kb=%d vb=%d" % (B, Hq, Hkv, ctx, nq, d, kb, vb))
+    _run(B, Hq, Hkv, ctx, nq, d, kb, vb, seed=ctx + nq + d)
+
+
+def test_attend_heavy_tails():
+    say("attend Student-t(3) 8x2 heads ctx 5000")
+    _run(1, 8, 2, 5000, 1, 128, 4, 4, seed=11, dist="t")
+
+
+def test_attend_esm2_bidirectional_slice():
+    say("attend esm2 layer 0 batch 0: 20 heads, 1024 queries x 1024 keys, d 64, RoPE q and k")
+    p = synth.esm2_params()
+    lay = synth.esm2_layer(p, 0, device="cuda", batch=1)
+    kc = tq.Codec(64, tq.TQ_PROD, 3, p["codec"].flip, p["codec"].S)
+    vc = tq.Codec(64, tq.TQ_MSE, 3, p["codec"].flip)
+    kpk, vpk = tq.encode_kv(kc, vc, lay["k"], lay["v"], rope=(10000.0, 1024))
+    out = tq.attend_decode(kc, vc, lay["q"], kpk, vpk, 1024, 20, rope=(10000.0, 0))
+    torch.cuda.synchronize()
+    q = to_np(lay["q"])
+    ref_out, _ = _oracle_attention(q, kpk, vpk, kc, vc, p["codec"], 1, 20, 1024,
+                                   q_rope_pos=np.arange(1024))
+    print("out max row rel err", check_rows(to_np(out), ref_out))
+
+
+def test_attend_llama_decode_slice():
+    say("attend llama layer 0: 8 q heads on 2 kv heads, ctx 131072, K prod b=3, V mse b=3")
+    p = synth.llama_prefill_params()
+    lay = synth.llama_prefill_layer(p, 0, device="cuda", heads=2)
+    kc = tq.Codec(128, tq.TQ_PROD, 3, p["codec"].flip, p["codec"].S)
+    vc = tq.Codec(128, tq.TQ_MSE, 3, p["codec"].flip)
+    kpk, vpk = tq.encode_kv(kc, vc, lay["k"].contiguous(), lay["v"].contiguous())
+    q = lay["q"][:8].reshape(1, 8, 1, 128).contiguous()
+    out, sc = tq.attend_decode(kc, vc, q, kpk, vpk, 131072, 2, want_scores=True)
+    torch.cuda.synchronize()
+    ref_out, ref_sc = _oracle_attention(to_np(q), kpk, vpk, kc, vc, p["codec"], 1, 2, 131072)
+    print("scores", check_rows(to_np(sc), ref_sc), "out", check_rows(to_np(out), ref_out))
