@@ -1,0 +1,688 @@
+// Decode attention straight from packed codes, few query rows per KV head
+// (GQA decode: the G query heads of one KV head at one position).
+//
+// "TurboESM", "2. Metodologia" part E (one pass: unpack, correct, attend
+// with an online softmax, no dequantized copy); "Google presenta TurboQuant",
+// "Eliminación del sesgo interno del producto" (the unbiased estimate):
+//   s_j = scale nu_j ( <q_rot, c_K[idx_j]> + sqrt(pi/2)/m gamma_j <Sq, 2 sigma_j - 1> )
+//   o   = Pi_V^T sum_j softmax(s)_j nu^V_j c_V[idx^V_j]
+//
+// decode_kernel: a workgroup (8 waves) owns one (batch, KV head), up to 4
+// query rows of it and one token range.  Set-up, all in LDS: the query rows
+// are rotated (q' = RoPE(q), q_rot = H (D_K q') / sqrt(d)), S is staged with
+// a padded stride for Sq = S q_rot, and three lookup tables are built that
+// replace per-coordinate multiplies in the scan:
+//   LK[f][v] = sum over the gk coordinates of field f of q_rot[i] c_K[code_i]
+//              (float4: the 4 rows), one entry per value v of a gk-code field;
+//   LQ[p][v] = sum_{b : bit b of v} Sq[8p + b]  (float4), per QJL byte value;
+//   LV[v]    = (c_V[v & mask], c_V[v >> CBV])  (float2), per pair of V codes.
+// Scan: scores with one token per lane (d/gk + m/8 table reads, float4 adds);
+// value sum with lane (cg, ts) owning coordinates 8cg..8cg+7 of tokens
+// ts + TS t (32 accumulators: 8 coordinates x 4 rows), fed by softmax
+// weights passed through LDS.  Running max per wave, running sums per lane.
+// The next tile's codes are loaded while the current one is processed.
+// The waves merge in LDS and the workgroup writes (acc, max, sum) per row.
+// merge_kernel: per query row, log-sum-exp merge of the token ranges and
+// o = D_V * H acc / sqrt(d), once per row (the rotation is linear).
+
+#include <cmath>
+
+#include "device_common.hpp"
+#include "internal.hpp"
+
+namespace tqk {
+
+constexpr int kDecWaves = 12;
+constexpr int kDecThreads = kDecWaves * kWave;
+constexpr int kDecRows = 4;
+
+struct DecodeParams {
+  const void* q;          // [batch][hq][n_q][D]
+  int q_f16;
+  const uint8_t* kidx;
+  const uint8_t* kqjl;
+  const float* knorm;
+  const float* krnorm;
+  const uint8_t* vidx;
+  const float* vnorm;
+  const float* S;         // m x D row-major
+  float* scores_out;      // optional [batch][hq][n_q][ctx]
+  float* part;            // [bg][chunk][split][kDecRows][D + 2]
+  int64_t ctx;
+  int batch, hq, hkv, n_q, G, nchunks, splits;
+  int64_t split_len;
+  float scale;
+  float qjl_scale;
+  float inv_sqrt_d;
+  int rope;
+  int32_t pos0;
+  float kcent[16];
+  float vcent[16];
+  uint32_t kflip[48];
+  double theta[64];
+};
+
+template <int CB>
+struct KGroup {
+  // coordinates per K table field
+  static constexpr int gk = CB == 1 ? 8 : (CB == 4 ? 1 : 2);
+  static constexpr int bits = gk * CB;
+  static constexpr int entries = 1 << bits;
+};
+
+template <int W>
+__device__ __forceinline__ uint32_t field_bits(const uint32_t (&w)[W], int off, int nbits) {
+  const int word = off >> 5, sh = off & 31;
+  uint32_t v;
+  if (sh + nbits <= 32) {
+    v = w[word] >> sh;
+  } else {
+    v = __builtin_amdgcn_alignbit(w[word + 1], w[word], sh);
+  }
+  return nbits == 32 ? v : (v & ((1u << nbits) - 1u));
+}
+
+__device__ __forceinline__ float4 f4add(float4 a, float4 b) {
+  return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+}
+
+__device__ __forceinline__ float4 f4fma(float4 a, float s, float4 c) {
+  return make_float4(fmaf(a.x, s, c.x), fmaf(a.y, s, c.y), fmaf(a.z, s, c.z), fmaf(a.w, s, c.w));
+}
+
+// Cross-lane moves inside each row of 16 lanes (DPP, no LDS traffic):
+// quad xor 1, quad xor 2, half-row mirror, row mirror.  After the four steps
+// every lane of a row holds the row's reduction; the four rows are combined
+// through scalar reads of one lane each, so every lane gets the same value.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  v = fmaxf(v, dpp_f<0x140>(v));
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  v += dpp_f<0x140>(v);
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (a + b) + (c + d);
+}
+
+template <int D, int CBK, int CBV>
+struct DecGeom {
+  using KG = KGroup<CBK>;
+  static constexpr int NF = D / KG::gk;          // K table fields per row
+  static constexpr int NE = KG::entries;
+  static constexpr int NB = D / 8;               // QJL bytes per row (m = D)
+  static constexpr int WK = D * CBK / 32;
+  static constexpr int KROW = D * CBK / 8;
+  static constexpr int KALIGN = KROW % 16 == 0 ? 16 : 8;
+  static constexpr int VW = D * CBV / 32;
+  static constexpr int VROW = D * CBV / 8;
+  static constexpr int NVE = 1 << (2 * CBV);
+  static constexpr int CG = D / 8;               // 8-coordinate groups of a V row
+  static constexpr int TS = kWave / CG;          // token subgroups per wave
+  static constexpr int TPL = kWave / TS;         // tokens per lane per tile
+  // LDS carve-up (bytes)
+  static constexpr int LK_B = NF * NE * 16;
+  static constexpr int LQ_B = NB * 256 * 16;
+  static constexpr int MRG_B = kDecWaves * kDecRows * (D + 2) * 4;   // wave merge
+  static constexpr int SQP_B = kDecThreads * 16;                      // Sq partials
+  static constexpr int TAB0_B = (LK_B + LQ_B) > SQP_B ? (LK_B + LQ_B) : SQP_B;
+  static constexpr int TAB_B = TAB0_B > MRG_B ? TAB0_B : MRG_B;
+  static constexpr int LV_B = NVE * 8;
+  static constexpr int W_B = kDecWaves * kWave * 16;
+  static constexpr int NIB_B = NB * 2 * 16 * 16;  // nibble sums, set-up only
+  static constexpr int WN_B = W_B > NIB_B ? W_B : NIB_B;
+};
+
+// One tile of a wave's token range: the key codes one lane needs.
+template <int WK, int NB4>
+struct TileRegs {
+  uint32_t kw[WK];
+  uint32_t sb[NB4];
+  float nuk, gk, nuv;
+};
+
+template <int D, int CBK, int CBV>
+__global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeParams p) {
+  using Gm = DecGeom<D, CBK, CBV>;
+  using KG = typename Gm::KG;
+  constexpr int NF = Gm::NF, NE = Gm::NE, NB = Gm::NB, WK = Gm::WK, KROW = Gm::KROW;
+  constexpr int VW = Gm::VW, VROW = Gm::VROW, NVE = Gm::NVE, CG = Gm::CG, TS = Gm::TS;
+  constexpr int TPL = Gm::TPL;
+  static_assert(CG * TS == kWave, "lane layout");
+
+  __shared__ __align__(16) unsigned char s_tab[Gm::TAB_B];   // LK | LQ  (Sq partials in set-up)
+  __shared__ __align__(16) float2 s_lv[NVE];
+  __shared__ __align__(16) unsigned char s_wn[Gm::WN_B];     // weights (nibble sums in set-up)
+  __shared__ __align__(16) float4 s_qT[D];                    // q_rot, 4 rows per coordinate
+  __shared__ __align__(16) float4 s_sT[D];                    // Sq, 4 rows per coordinate
+  __shared__ float s_qr[kDecRows][D];
+  __shared__ float s_tot[kDecRows];
+  __shared__ float s_kc[16], s_vc[16];
+  __shared__ uint32_t s_kflip[D / 32];
+  __shared__ double s_theta[D / 2];
+
+  float4* s_lk = reinterpret_cast<float4*>(s_tab);
+  float4* s_lq = reinterpret_cast<float4*>(s_tab + Gm::LK_B);
+  float4* s_w = reinterpret_cast<float4*>(s_wn);               // [wave][lane]
+  float4* s_nib = reinterpret_cast<float4*>(s_wn);             // [byte][half][16]
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int bgc = blockIdx.x;                    // (batch * hkv) * nchunks + chunk
+  const int split = blockIdx.y;
+  const int bg = bgc / p.nchunks, chunk = bgc % p.nchunks;
+  const int b = bg / p.hkv, g = bg % p.hkv;
+  const int qr_total = p.G * p.n_q;
+  const int lr0 = chunk * kDecRows;
+  const int nrows = (qr_total - lr0) < kDecRows ? (qr_total - lr0) : kDecRows;
+  const int64_t row_base = ((int64_t)b * p.hq + (int64_t)g * p.G) * p.n_q + lr0;
+  const int64_t t0 = (int64_t)split * p.split_len;
+  int64_t t1 = t0 + p.split_len;
+  if (t1 > p.ctx) t1 = p.ctx;
+  const int64_t kv_base = (int64_t)bg * p.ctx;
+  const int cg = lane % CG, ts = lane / CG;
+  const int vbit0 = cg * 8 * CBV;
+  const int vw0 = vbit0 >> 5;
+  const int vw1 = (vw0 + 1) < VW ? (vw0 + 1) : (VW - 1);
+  const bool vstraddle = (vbit0 & 31) + 8 * CBV > 32;
+
+  auto load_tile = [&](int64_t tile, TileRegs<WK, NB / 4>& R) {
+    const int64_t tok = tile + lane;
+    const int64_t kr = kv_base + (tok < t1 ? tok : t0);
+    load_words<WK, Gm::KALIGN>(p.kidx + kr * KROW, R.kw);
+    load_words<NB / 4, (NB % 16 == 0) ? 16 : 8>(p.kqjl + kr * NB, R.sb);
+    R.nuk = p.knorm[kr] * p.scale;
+    R.gk = p.krnorm[kr] * p.qjl_scale;
+    R.nuv = p.vnorm[kr];
+  };
+
+  // first tile's key codes in flight during the set-up
+  TileRegs<WK, NB / 4> cur;
+  const int64_t first = t0 + (int64_t)wave * kWave;
+  if (first < t1) load_tile(first, cur);
+
+  // ---- set-up ----
+  // S rows for Sq, straight into registers: thread -> (coordinate i, k-part)
+  constexpr int KP = (kDecThreads / D) >= 8 ? 8 : ((kDecThreads / D) >= 4 ? 4 : 2);  // k-parts
+  constexpr int KL = D / KP;                      // k per part
+  const int si = tid % D, spart = tid / D;
+  const bool sq_thread = spart < KP;
+  float4 srow[KL / 4];
+  if (sq_thread) {
+    const float4* S4 = reinterpret_cast<const float4*>(p.S + (size_t)si * D + spart * KL);
+#pragma unroll
+    for (int j = 0; j < KL / 4; ++j) srow[j] = S4[j];
+  }
+  const DecodeParams* kp = (const DecodeParams*)__builtin_amdgcn_kernarg_segment_ptr();
+  if (tid < 16) {
+    s_kc[tid] = kp->kcent[tid];
+    s_vc[tid] = kp->vcent[tid];
+  }
+  if (tid >= 64 && tid < 64 + D / 32) s_kflip[tid - 64] = kp->kflip[tid - 64];
+  if (tid >= 128 && tid < 128 + D / 2) s_theta[tid - 128] = kp->theta[tid - 128];
+  constexpr int PER = (kDecRows * D + kDecThreads - 1) / kDecThreads;
+  for (int t = tid; t < kDecRows * D; t += kDecThreads) {
+    const int r = t / D, i = t % D;
+    float v = 0.f;
+    if (r < nrows) {
+      const int64_t off = (row_base + r) * D + i;
+      v = p.q_f16 ? (float)reinterpret_cast<const _Float16*>(p.q)[off]
+                  : reinterpret_cast<const float*>(p.q)[off];
+    }
+    s_qr[r][i] = v;
+  }
+  __syncthreads();
+  // q' = RoPE(q), sign flip, natural-order butterflies through LDS
+  float qv[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int t = tid + u * kDecThreads;
+    qv[u] = 0.f;
+    if (t < kDecRows * D) {
+      const int r = t / D, i = t % D;
+      float x = s_qr[r][i];
+      if (p.rope) {
+        const int pr = i >> 1;
+        const int64_t pos = (int64_t)p.pos0 + ((lr0 + r) % p.n_q);
+        float sn, cs;
+        sincos_reduced((double)pos * s_theta[pr], sn, cs);
+        const float a = s_qr[r][2 * pr], bb = s_qr[r][2 * pr + 1];
+        x = (i & 1) ? (a * sn + bb * cs) : (a * cs - bb * sn);
+      }
+      const uint32_t bit = (s_kflip[i >> 5] >> (i & 31)) & 1u;
+      qv[u] = bit ? -x : x;
+    }
+  }
+  for (int h = 1; h < D; h <<= 1) {
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int t = tid + u * kDecThreads;
+      if (t < kDecRows * D) s_qr[t / D][t % D] = qv[u];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int t = tid + u * kDecThreads;
+      if (t < kDecRows * D) {
+        const int r = t / D, i = t % D;
+        const float o = s_qr[r][i ^ h];
+        qv[u] = (i & h) ? (o - qv[u]) : (qv[u] + o);
+      }
+    }
+  }
+  // q_rot, 4 rows per coordinate
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int t = tid + u * kDecThreads;
+    if (t < kDecRows * D)
+      reinterpret_cast<float*>(s_qT)[4 * (t % D) + t / D] = qv[u] * p.inv_sqrt_d;
+  }
+  __syncthreads();
+  // Sq partial sums over this thread's k-part, then a reduction over parts
+  if (sq_thread) {
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < KL / 4; ++j) {
+      const int k = spart * KL + 4 * j;
+      a = f4fma(s_qT[k], srow[j].x, a);
+      a = f4fma(s_qT[k + 1], srow[j].y, a);
+      a = f4fma(s_qT[k + 2], srow[j].z, a);
+      a = f4fma(s_qT[k + 3], srow[j].w, a);
+    }
+    reinterpret_cast<float4*>(s_tab)[spart * D + si] = a;
+  }
+  __syncthreads();
+  if (tid < D) {
+    float4 a = reinterpret_cast<const float4*>(s_tab)[tid];
+#pragma unroll
+    for (int q = 1; q < KP; ++q) a = f4add(a, reinterpret_cast<const float4*>(s_tab)[q * D + tid]);
+    s_sT[tid] = a;
+  }
+  __syncthreads();
+  // tot[r] = sum_i Sq[r][i]: one wave per row
+  if (wave < kDecRows) {
+    float t = 0.f;
+    for (int i = lane; i < D; i += kWave) t += reinterpret_cast<const float*>(s_sT)[4 * i + wave];
+    t = wave_sum(t);
+    if (lane == 0) s_tot[wave] = t;
+  }
+  // nibble sums of Sq for the QJL byte table: (byte pb, half h, nibble n)
+  for (int t = tid; t < NB * 32; t += kDecThreads) {
+    const int pb = t >> 5, h = (t >> 4) & 1, n = t & 15;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if ((n >> e) & 1) a = f4add(a, s_sT[8 * pb + 4 * h + e]);
+    s_nib[t] = a;
+  }
+  // LK: lanes over table values (this thread's centroids stay in registers)
+  {
+    for (int t = tid; t < NF * NE; t += kDecThreads) {
+      const int v = t % NE, f = t / NE;
+      float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int e = 0; e < KG::gk; ++e)
+        a = f4fma(s_qT[f * KG::gk + e], s_kc[(v >> (e * CBK)) & ((1 << CBK) - 1)], a);
+      s_lk[t] = a;
+    }
+  }
+  for (int t = tid; t < NVE; t += kDecThreads)
+    s_lv[t] = make_float2(s_vc[t & ((1 << CBV) - 1)], s_vc[t >> CBV]);
+  __syncthreads();
+  for (int t = tid; t < NB * 256; t += kDecThreads) {
+    const int pb = t >> 8, v = t & 255;
+    s_lq[t] = f4add(s_nib[pb * 32 + (v & 15)], s_nib[pb * 32 + 16 + (v >> 4)]);
+  }
+  __syncthreads();
+  const float4 tot = make_float4(s_tot[0], s_tot[1], s_tot[2], s_tot[3]);
+
+  // ---- scan of the token range ----
+  float m_run[kDecRows], l_run[kDecRows];
+  float acc[kDecRows][8];
+#pragma unroll
+  for (int r = 0; r < kDecRows; ++r) {
+    m_run[r] = -INFINITY;
+    l_run[r] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[r][e] = 0.f;
+  }
+  const float4* __restrict__ lk = s_lk;
+  const float4* __restrict__ lq = s_lq;
+
+  for (int64_t tile = first; tile < t1; tile += (int64_t)kDecWaves * kWave) {
+    const TileRegs<WK, NB / 4> R = cur;
+    const int64_t next = tile + (int64_t)kDecWaves * kWave;
+    if (next < t1) load_tile(next, cur);
+    const int64_t tok = tile + lane;
+    const bool valid = tok < t1;
+    // this tile's value codes (used after the scores)
+    uint32_t vwr[TPL][2];
+#pragma unroll
+    for (int u = 0; u < TPL; ++u) {
+      int64_t vt = tile + (int64_t)u * TS + ts;
+      vt = vt < t1 ? vt : t0;
+      const uint32_t* vr = reinterpret_cast<const uint32_t*>(p.vidx + (kv_base + vt) * VROW);
+      vwr[u][0] = vr[vw0];
+      vwr[u][1] = vstraddle ? vr[vw1] : 0u;
+    }
+
+    // four independent accumulation chains per table
+    float4 msa[4] = {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f),
+                     make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const uint32_t v = field_bits<WK>(R.kw, f * KG::bits, KG::bits);
+      msa[f & 3] = f4add(msa[f & 3], lk[f * NE + v]);
+      // bound the table reads in flight (each holds 4 registers)
+      if ((f & 15) == 15) __builtin_amdgcn_sched_barrier(0);
+    }
+    float4 qsa[2] = {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
+#pragma unroll
+    for (int pb = 0; pb < NB; ++pb) {
+      const uint32_t v = (R.sb[pb >> 2] >> (8 * (pb & 3))) & 255u;
+      qsa[pb & 1] = f4add(qsa[pb & 1], lq[pb * 256 + v]);
+    }
+    const float4 ms = f4add(f4add(msa[0], msa[1]), f4add(msa[2], msa[3]));
+    const float4 qs = f4add(qsa[0], qsa[1]);
+    float s[kDecRows];
+    s[0] = R.nuk * fmaf(R.gk, 2.f * qs.x - tot.x, ms.x);
+    s[1] = R.nuk * fmaf(R.gk, 2.f * qs.y - tot.y, ms.y);
+    s[2] = R.nuk * fmaf(R.gk, 2.f * qs.z - tot.z, ms.z);
+    s[3] = R.nuk * fmaf(R.gk, 2.f * qs.w - tot.w, ms.w);
+    if (p.scores_out != nullptr && valid) {
+#pragma unroll
+      for (int r = 0; r < kDecRows; ++r)
+        if (r < nrows) p.scores_out[(row_base + r) * p.ctx + tok] = s[r];
+    }
+    float pw[kDecRows];
+#pragma unroll
+    for (int r = 0; r < kDecRows; ++r) {
+      const float sv = valid ? s[r] : -INFINITY;
+      const float mt = wave_max(sv);
+      const float mn = fmaxf(m_run[r], mt);
+      const float alpha = __expf(m_run[r] - mn);
+      m_run[r] = mn;
+      const float e = valid ? __expf(sv - mn) : 0.f;
+      l_run[r] = fmaf(l_run[r], alpha, e);
+      pw[r] = e * R.nuv;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[r][k] *= alpha;
+    }
+    s_w[wave * kWave + lane] = make_float4(pw[0], pw[1], pw[2], pw[3]);
+    // LDS operations of one wave complete in order: the weights written
+    // above are visible to the reads below without a workgroup barrier.
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int u = 0; u < TPL; ++u) {
+      const float4 w = s_w[wave * kWave + u * TS + ts];
+      const uint32_t bits = vstraddle
+                                ? __builtin_amdgcn_alignbit(vwr[u][1], vwr[u][0], vbit0 & 31)
+                                : (vwr[u][0] >> (vbit0 & 31));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t pv = (bits >> (2 * CBV * e)) & (NVE - 1);
+        const float2 c2 = s_lv[pv];
+        acc[0][2 * e] = fmaf(w.x, c2.x, acc[0][2 * e]);
+        acc[0][2 * e + 1] = fmaf(w.x, c2.y, acc[0][2 * e + 1]);
+        acc[1][2 * e] = fmaf(w.y, c2.x, acc[1][2 * e]);
+        acc[1][2 * e + 1] = fmaf(w.y, c2.y, acc[1][2 * e + 1]);
+        acc[2][2 * e] = fmaf(w.z, c2.x, acc[2][2 * e]);
+        acc[2][2 * e + 1] = fmaf(w.z, c2.y, acc[2][2 * e + 1]);
+        acc[3][2 * e] = fmaf(w.w, c2.x, acc[3][2 * e]);
+        acc[3][2 * e + 1] = fmaf(w.w, c2.y, acc[3][2 * e + 1]);
+      }
+      if ((u & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // ---- merge the waves, write this range's (acc, max, sum) per row ----
+#pragma unroll
+  for (int r = 0; r < kDecRows; ++r) {
+    l_run[r] = wave_sum(l_run[r]);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+#pragma unroll
+      for (int off = CG; off < kWave; off <<= 1) acc[r][k] += __shfl_xor(acc[r][k], off);
+    }
+  }
+  __syncthreads();   // tables are no longer read: reuse them as merge space
+  constexpr int REC = D + 2;
+  float* mrg = reinterpret_cast<float*>(s_tab);   // [wave][row][D + 2]
+  if (ts == 0) {
+#pragma unroll
+    for (int r = 0; r < kDecRows; ++r)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) mrg[(wave * kDecRows + r) * REC + 8 * cg + k] = acc[r][k];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < kDecRows; ++r) {
+      mrg[(wave * kDecRows + r) * REC + D] = m_run[r];
+      mrg[(wave * kDecRows + r) * REC + D + 1] = l_run[r];
+    }
+  }
+  __syncthreads();
+  const int64_t rec0 = ((int64_t)bgc * p.splits + split) * kDecRows;
+  for (int t = tid; t < kDecRows * D; t += kDecThreads) {
+    const int r = t / D, i = t % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, mrg[(w * kDecRows + r) * REC + D]);
+    float a = 0.f, L = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) {
+      const float mw = mrg[(w * kDecRows + r) * REC + D];
+      const float f = mw == -INFINITY ? 0.f : __expf(mw - M);
+      a = fmaf(mrg[(w * kDecRows + r) * REC + i], f, a);
+      L = fmaf(mrg[(w * kDecRows + r) * REC + D + 1], f, L);
+    }
+    float* rec = p.part + (rec0 + r) * REC;
+    rec[i] = a;
+    if (i == 0) {
+      rec[D] = M;
+      rec[D + 1] = L;
+    }
+  }
+}
+
+struct MergeParams {
+  const float* part;
+  float* out;
+  int hq, hkv, n_q, G, nchunks, splits;
+  float inv_sqrt_d;
+  uint32_t vflip[48];
+};
+
+// Log-sum-exp merge of the token ranges of one query row, then
+// o = D_V * (H a) / sqrt(d).
+template <int D>
+__global__ __launch_bounds__(D) void merge_kernel(MergeParams p) {
+  constexpr int REC = D + 2;
+  constexpr int CH = 2 * D < 128 ? 2 * D : 128;  // (max, sum) pairs staged per pass
+  __shared__ float s_v[D];
+  __shared__ float s_ml[CH];
+  const int i = threadIdx.x;
+  const int64_t row = blockIdx.x;                 // (b, h, a)
+  const int a = (int)(row % p.n_q);
+  const int64_t bh = row / p.n_q;
+  const int h = (int)(bh % p.hq);
+  const int b = (int)(bh / p.hq);
+  const int g = h / p.G;
+  const int lr = (h - g * p.G) * p.n_q + a;
+  const int chunk = lr / kDecRows, r = lr % kDecRows;
+  const int64_t bgc = ((int64_t)b * p.hkv + g) * p.nchunks + chunk;
+  const float* base = p.part + (bgc * p.splits * kDecRows + r) * REC;
+  const int64_t stride = (int64_t)kDecRows * REC;
+  float M = -INFINITY, L = 0.f, v = 0.f;
+  for (int s0 = 0; s0 < p.splits; s0 += CH / 2) {
+    const int ns = (p.splits - s0) < CH / 2 ? (p.splits - s0) : CH / 2;
+    __syncthreads();
+    for (int t = i; t < 2 * ns; t += D) s_ml[t] = base[(s0 + (t >> 1)) * stride + D + (t & 1)];
+    __syncthreads();
+    float Mc = M;
+    for (int s = 0; s < ns; ++s) Mc = fmaxf(Mc, s_ml[2 * s]);
+    const float rescale = M == -INFINITY ? 0.f : __expf(M - Mc);
+    L *= rescale;
+    v *= rescale;
+    int s = 0;
+    for (; s + 32 <= ns; s += 32) {
+      float x[32];     // all loads of the chunk in flight together
+#pragma unroll
+      for (int u = 0; u < 32; ++u) x[u] = base[(s0 + s + u) * stride + i];
+#pragma unroll
+      for (int u = 0; u < 32; ++u) {
+        const float ms = s_ml[2 * (s + u)];
+        const float f = ms == -INFINITY ? 0.f : __expf(ms - Mc);
+        v = fmaf(x[u], f, v);
+        L = fmaf(s_ml[2 * (s + u) + 1], f, L);
+      }
+    }
+    for (; s < ns; ++s) {
+      const float ms = s_ml[2 * s];
+      const float f = ms == -INFINITY ? 0.f : __expf(ms - Mc);
+      v = fmaf(base[(s0 + s) * stride + i], f, v);
+      L = fmaf(s_ml[2 * s + 1], f, L);
+    }
+    M = Mc;
+  }
+  v /= L;
+#pragma unroll
+  for (int hh = 1; hh < D; hh <<= 1) {
+    __syncthreads();
+    s_v[i] = v;
+    __syncthreads();
+    const float o = s_v[i ^ hh];
+    v = (i & hh) ? (o - v) : (v + o);
+  }
+  const uint32_t bit = (p.vflip[i >> 5] >> (i & 31)) & 1u;
+  v *= p.inv_sqrt_d;
+  p.out[row * D + i] = bit ? -v : v;
+}
+
+// ---------------------------------------------------------------------------
+
+static void plan_decode(int batch, int n_q, int hq, int hkv, int64_t ctx, int& nchunks,
+                        int& splits, int64_t& split_len) {
+  const int G = hq / hkv;
+  nchunks = (G * n_q + kDecRows - 1) / kDecRows;
+  const int64_t groups = (int64_t)batch * hkv * nchunks;
+  const int64_t tiles = (ctx + kWave - 1) / kWave;
+  const int cus = device_cu_count();
+  int64_t want = (cus + groups - 1) / groups;
+  if (want > tiles) want = tiles;
+  if (want < 1) want = 1;
+  split_len = ((ctx + want - 1) / want + kWave - 1) / kWave * kWave;
+  splits = (int)((ctx + split_len - 1) / split_len);
+}
+
+bool decode_path(int n_q, int hq, int hkv) {
+  return (hq / hkv) * n_q <= 16;
+}
+
+size_t decode_workspace_bytes(int batch, int n_q, int hq, int hkv, int64_t ctx, int d) {
+  int nchunks, splits;
+  int64_t split_len;
+  plan_decode(batch, n_q, hq, hkv, ctx, nchunks, splits, split_len);
+  const size_t groups = (size_t)batch * hkv * nchunks;
+  return groups * splits * kDecRows * (d + 2) * sizeof(float);
+}
+
+template <int D, int CBK, int CBV>
+static hipError_t run_decode(const DecodeParams& p, dim3 grid, hipStream_t s) {
+  hipLaunchKernelGGL((decode_kernel<D, CBK, CBV>), grid, dim3(kDecThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int D, int CBK>
+static hipError_t dec_pick_v(int cbv, const DecodeParams& p, dim3 grid, hipStream_t s) {
+  switch (cbv) {
+    case 1: return run_decode<D, CBK, 1>(p, grid, s);
+    case 2: return run_decode<D, CBK, 2>(p, grid, s);
+    case 3: return run_decode<D, CBK, 3>(p, grid, s);
+    case 4: return run_decode<D, CBK, 4>(p, grid, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int D>
+static hipError_t dec_pick_k(int cbk, int cbv, const DecodeParams& p, dim3 grid, hipStream_t s) {
+  switch (cbk) {
+    case 1: return dec_pick_v<D, 1>(cbv, p, grid, s);
+    case 2: return dec_pick_v<D, 2>(cbv, p, grid, s);
+    case 3: return dec_pick_v<D, 3>(cbv, p, grid, s);
+    case 4: return dec_pick_v<D, 4>(cbv, p, grid, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode(const tq_codec& kc, const tq_codec& vc, const void* q, int q_dtype,
+                         int batch, int n_q, int hq, int hkv, const RopeHost& rope,
+                         const tq_packed& k, const tq_packed& v, int64_t ctx, float scale,
+                         float* out, float* scores_out, void* workspace, hipStream_t stream) {
+  const int d = kc.d;
+  int nchunks, splits;
+  int64_t split_len;
+  plan_decode(batch, n_q, hq, hkv, ctx, nchunks, splits, split_len);
+  const size_t groups = (size_t)batch * hkv * nchunks;
+  DecodeParams p = {};
+  p.q = q;
+  p.q_f16 = q_dtype == TQ_F16;
+  p.kidx = k.idx; p.kqjl = k.qjl; p.knorm = k.norm; p.krnorm = k.rnorm;
+  p.vidx = v.idx; p.vnorm = v.norm;
+  p.S = kc.S;
+  p.scores_out = scores_out;
+  p.part = reinterpret_cast<float*>(workspace);
+  p.ctx = ctx; p.batch = batch; p.hq = hq; p.hkv = hkv; p.n_q = n_q; p.G = hq / hkv;
+  p.nchunks = nchunks; p.splits = splits; p.split_len = split_len;
+  p.scale = scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)d));
+  p.qjl_scale = (float)(std::sqrt(M_PI / 2.0) / kc.m);
+  p.inv_sqrt_d = (float)(1.0 / std::sqrt((double)d));
+  p.rope = rope.on ? 1 : 0;
+  p.pos0 = rope.on ? rope.pos0 : 0;
+  for (int i = 0; i < 16; ++i) { p.kcent[i] = kc.centroids[i]; p.vcent[i] = vc.centroids[i]; }
+  for (int w = 0; w < 48; ++w) p.kflip[w] = kc.flip[w];
+  if (rope.on)
+    for (int i = 0; i < d / 2 && i < 64; ++i)
+      p.theta[i] = std::pow((double)rope.base, -2.0 * i / (double)d);
+  const dim3 grid((unsigned)groups, (unsigned)splits);
+  hipError_t e;
+  if (d == 128) e = dec_pick_k<128>(kc.code_bits, vc.code_bits, p, grid, stream);
+  else if (d == 64) e = dec_pick_k<64>(kc.code_bits, vc.code_bits, p, grid, stream);
+  else return hipErrorInvalidValue;
+  if (e != hipSuccess) return e;
+  MergeParams mp = {};
+  mp.part = p.part;
+  mp.out = out;
+  mp.hq = hq; mp.hkv = hkv; mp.n_q = n_q; mp.G = hq / hkv; mp.nchunks = nchunks;
+  mp.splits = splits;
+  mp.inv_sqrt_d = p.inv_sqrt_d;
+  for (int w = 0; w < 48; ++w) mp.vflip[w] = vc.flip[w];
+  const unsigned rows = (unsigned)((int64_t)batch * hq * n_q);
+  if (d == 128)
+    hipLaunchKernelGGL((merge_kernel<128>), dim3(rows), dim3(128), 0, stream, mp);
+  else
+    hipLaunchKernelGGL((merge_kernel<64>), dim3(rows), dim3(64), 0, stream, mp);
+  return hipGetLastError();
+}
+
+}  // namespace tqk

@@ -29,6 +29,13 @@ hipError_t launch_attend(const tq_codec& kc, const tq_codec& vc, const void* q,
                          float* out, float* scores_out, void* workspace,
                          hipStream_t stream);
 
+bool decode_path(int n_q, int hq, int hkv);
+size_t decode_workspace_bytes(int batch, int n_q, int hq, int hkv, int64_t ctx, int d);
+hipError_t launch_decode(const tq_codec& kc, const tq_codec& vc, const void* q, int q_dtype,
+                         int batch, int n_q, int hq, int hkv, const RopeHost& rope,
+                         const tq_packed& k, const tq_packed& v, int64_t ctx, float scale,
+                         float* out, float* scores_out, void* workspace, hipStream_t stream);
+
 size_t scan_workspace_bytes(int64_t n_q, int64_t n, int d, int top_k);
 hipError_t launch_scan(const tq_codec& c, const void* q, int q_dtype,
                        int64_t n_q, const tq_packed& x, int64_t n, float* out,

@@ -1,9 +1,15 @@
 // Query preparation shared by attention and the inner-product scan:
 //   q' = RoPE(q) (optional), q_rot = H_d (D * q') / sqrt(d), Sq = S q_rot.
-// The query is not normalised: the estimate of <q, x> is linear in q
-// ("Google presenta TurboQuant ...", "Eliminación del sesgo interno del
-// producto").  One workgroup of d threads per query row; the butterflies
-// run through LDS, the S q_rot rows are d-long dot products.
+// The query is not normalised: the
+// estimate of <q, x> is linear in q ("Google presenta TurboQuant ...",
+// "Eliminación del sesgo interno del producto").
+//
+// A workgroup prepares kQRows query rows: their butterflies run through
+// LDS, and S is staged once into LDS with a padded row stride (d + 1
+// floats, so that the lanes of a wave reading S[i][k] for consecutive i hit
+// distinct banks) and read from there for the d-long dot products.
+
+#include <cmath>
 
 #include "device_common.hpp"
 #include "internal.hpp"
@@ -11,60 +17,118 @@
 
 namespace tqk {
 
+constexpr int kQRows = 8;
+constexpr int kQThreads = 256;
+
 template <int D, typename T, bool ROPE>
-__global__ __launch_bounds__(D) void qprep_kernel(QPrepParams p) {
-  __shared__ float s_v[D];
-  const int i = threadIdx.x;
-  const int64_t row = blockIdx.x;
-  const T* q = reinterpret_cast<const T*>(p.q) + row * D;
-  float v = (float)q[i];
-  if constexpr (ROPE) {
-    s_v[i] = v;
-    __syncthreads();
-    const int pair = i >> 1;
-    const int64_t pos = (int64_t)p.pos0 + (row % p.n_q);
-    float s, c;
-    sincos_reduced((double)pos * p.theta[pair], s, c);
-    const float a = s_v[2 * pair], b = s_v[2 * pair + 1];
-    v = (i & 1) ? (a * s + b * c) : (a * c - b * s);
-    __syncthreads();
+__global__ __launch_bounds__(kQThreads) void qprep_kernel(QPrepParams p) {
+  constexpr int SP = D + 1;                         // padded S row stride
+  __shared__ float s_S[D * SP];
+  __shared__ float s_v[kQRows][D];
+  __shared__ uint32_t s_flip[D / 32];
+  __shared__ double s_theta[D / 2];
+
+  const int tid = threadIdx.x;
+  const int64_t row0 = (int64_t)blockIdx.x * kQRows;
+  const int nrows = (p.n_rows - row0) < kQRows ? (int)(p.n_rows - row0) : kQRows;
+  const uint32_t* kflip = reinterpret_cast<const uint32_t*>(
+      (const char*)__builtin_amdgcn_kernarg_segment_ptr() +
+      offsetof(QPrepParams, flip));
+  const double* ktheta = reinterpret_cast<const double*>(
+      (const char*)__builtin_amdgcn_kernarg_segment_ptr() +
+      offsetof(QPrepParams, theta));
+  if (tid < D / 32) s_flip[tid] = kflip[tid];
+  if (ROPE && tid < D / 2) s_theta[tid] = ktheta[tid];
+
+  // S into LDS (coalesced 16-byte reads, padded rows)
+  if (p.S != nullptr) {
+    const float4* S4 = reinterpret_cast<const float4*>(p.S);
+    for (int t = tid; t < D * D / 4; t += kQThreads) {
+      const float4 v = S4[t];
+      const int i = (4 * t) / D, k = (4 * t) % D;
+      float* dst = s_S + i * SP + k;
+      dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
+    }
   }
-  const uint32_t bit = (p.flip[i >> 5] >> (i & 31)) & 1u;
-  v = bit ? -v : v;
+  // query rows
+  const T* q = reinterpret_cast<const T*>(p.q);
+  for (int t = tid; t < kQRows * D; t += kQThreads) {
+    const int r = t / D, i = t % D;
+    s_v[r][i] = r < nrows ? (float)q[(row0 + r) * D + i] : 0.f;
+  }
+  __syncthreads();
+  constexpr int PER = kQRows * D / kQThreads;
+  float v[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int t = tid + u * kQThreads, r = t / D, i = t % D;
+    float x = s_v[r][i];
+    if constexpr (ROPE) {
+      const int pr = i >> 1;
+      const int64_t pos = (int64_t)p.pos0 + ((row0 + r) % p.n_q);
+      float sn, cs;
+      sincos_reduced((double)pos * s_theta[pr], sn, cs);
+      const float a = s_v[r][2 * pr], b = s_v[r][2 * pr + 1];
+      x = (i & 1) ? (a * sn + b * cs) : (a * cs - b * sn);
+    }
+    const uint32_t bit = (s_flip[i >> 5] >> (i & 31)) & 1u;
+    v[u] = bit ? -x : x;
+  }
   // natural-order butterflies through LDS
 #pragma unroll
   for (int h = 1; h < D; h <<= 1) {
-    s_v[i] = v;
     __syncthreads();
-    const float o = s_v[i ^ h];
-    v = (i & h) ? (o - v) : (v + o);
-    __syncthreads();
-  }
-  v *= p.inv_sqrt_d;
-  s_v[i] = v;
-  p.qrot[row * D + i] = v;
-  if (p.S != nullptr) {
-    __syncthreads();
-    const float4* srow = reinterpret_cast<const float4*>(p.S + (size_t)i * D);
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-    for (int k = 0; k < D / 4; ++k) {
-      const float4 s = srow[k];
-      acc[0] = fmaf(s.x, s_v[4 * k], acc[0]);
-      acc[1] = fmaf(s.y, s_v[4 * k + 1], acc[1]);
-      acc[2] = fmaf(s.z, s_v[4 * k + 2], acc[2]);
-      acc[3] = fmaf(s.w, s_v[4 * k + 3], acc[3]);
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int t = tid + u * kQThreads;
+      s_v[t / D][t % D] = v[u];
     }
-    p.sq[row * D + i] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int t = tid + u * kQThreads, r = t / D, i = t % D;
+      const float o = s_v[r][i ^ h];
+      v[u] = (i & h) ? (o - v[u]) : (v[u] + o);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int t = tid + u * kQThreads, r = t / D, i = t % D;
+    const float x = v[u] * p.inv_sqrt_d;
+    s_v[r][i] = x;
+    if (r < nrows) p.qrot[(row0 + r) * D + i] = x;
+  }
+  if (p.S == nullptr) return;
+  __syncthreads();
+  // Sq[r][i] = sum_k S[i][k] q_rot[r][k]; thread -> (row group, i)
+  constexpr int RG = kQThreads / D;                 // row groups (2 for d=128)
+  constexpr int RPG = kQRows / RG;                  // rows per group
+  const int i = tid % D, rg = tid / D;
+  float acc[RPG];
+#pragma unroll
+  for (int a = 0; a < RPG; ++a) acc[a] = 0.f;
+  const float* srow = s_S + i * SP;
+#pragma unroll 4
+  for (int k = 0; k < D; ++k) {
+    const float s = srow[k];
+#pragma unroll
+    for (int a = 0; a < RPG; ++a) acc[a] = fmaf(s, s_v[rg * RPG + a][k], acc[a]);
+  }
+#pragma unroll
+  for (int a = 0; a < RPG; ++a) {
+    const int r = rg * RPG + a;
+    if (r < nrows) p.sq[(row0 + r) * D + i] = acc[a];
   }
 }
 
 template <int D, typename T>
 static hipError_t run_qprep(const QPrepParams& p, bool rope, hipStream_t s) {
+  const unsigned blocks = (unsigned)((p.n_rows + kQRows - 1) / kQRows);
   if (rope)
-    hipLaunchKernelGGL((qprep_kernel<D, T, true>), dim3((unsigned)p.n_rows), dim3(D), 0, s, p);
+    hipLaunchKernelGGL((qprep_kernel<D, T, true>), dim3(blocks), dim3(kQThreads), 0, s, p);
   else
-    hipLaunchKernelGGL((qprep_kernel<D, T, false>), dim3((unsigned)p.n_rows), dim3(D), 0, s, p);
+    hipLaunchKernelGGL((qprep_kernel<D, T, false>), dim3(blocks), dim3(kQThreads), 0, s, p);
   return hipGetLastError();
 }
 
