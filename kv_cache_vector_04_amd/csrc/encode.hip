@@ -11,14 +11,31 @@
 // wave, done on the matrix cores with v_mfma_f32_32x32x16_f16 in three
 // passes S_hi r_hi + S_hi r_lo + S_lo r_hi (fp16 hi/lo splits of both
 // operands, fp32 accumulation), which keeps |error| of (S r)_i near 1e-7.
-// r is scaled by 2^8 before the split so that its low part stays a normal
-// fp16 number; the sign of S r does not change.
+// The prod path works with r' = 256 r (a power of two, so that the low
+// fp16 part of r' stays a normal number); the sign of S r' is that of S r.
+//
+// Quantizer: codes with 3 or more bits use a uniform grid over z in
+// [-1.01, 1.01] (u = a z + b, cell = floor(u)) with at most one threshold
+// per cell; a cell's entry holds the threshold inside it (u units) and the
+// number of thresholds below the cell, so the code is one table read and
+// one compare (the host picks the smallest grid with that property).  The
+// result equals #{k : u >= a t_k + b}, the code of z up to fp32 rounding.
+// One- and two-bit codes compare directly.
+//
+// fp16 input: the sign flip is an xor on the packed halves, the norm comes
+// from v_dot2 on them, and the first butterfly stage converts and adds in
+// one v_fma_mix_f32 per output.
 //
 // Layout of a wave's tile: lane l owns row 64*tile + l.  The MFMA B operand
 // for 32 tokens needs, in lane l, token l%32 and the k-group l/32; the two
 // 32-token blocks of a tile are exchanged between wave halves with one
-// v_permlane32_swap per packed register, and the sign words are put back on
-// their owning lanes the same way.
+// v_permlane32_swap per pair of packed registers.  The rows of S in the A
+// fragments are ordered so that the C registers of lane l hold rows
+// 16 (l/32) + 0..15 of the 32-row tile: each lane half collects 16
+// consecutive sign bits, and one more swap puts every word on its row.
+
+#include <cmath>
+#include <cstring>
 
 #include "device_common.hpp"
 #include "internal.hpp"
@@ -26,6 +43,8 @@
 namespace tqk {
 
 constexpr int kEncWaves = 8;
+constexpr int kLutMax = 256;
+constexpr float kGridRange = 1.01f;
 
 struct EncodeParams {
   const void* x;
@@ -36,6 +55,9 @@ struct EncodeParams {
   float* rnorm;
   CodecArgs codec;
   int64_t seq_len;
+  int lut_g;            // grid cells (codes of 3 or more bits)
+  float lut_a, lut_b;   // u = z a + b
+  uint32_t hflip[64];   // fp16 pairs: xor masks (bits 15, 31) of the sign flip
   double theta[64];
 };
 
@@ -51,6 +73,27 @@ __device__ __forceinline__ uint32_t pack_h2(_Float16 a, _Float16 b) {
          ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
+// lo + hi and lo - hi of the two fp16 halves of w, in fp32
+__device__ __forceinline__ void mix_butterfly(uint32_t w, float& s, float& d) {
+  asm("v_fma_mix_f32 %0, %1, 1.0, %1 op_sel:[0,0,1] op_sel_hi:[1,0,1]" : "=v"(s) : "v"(w));
+  asm("v_fma_mix_f32 %0, %1, 1.0, -%1 op_sel:[0,0,1] op_sel_hi:[1,0,1]" : "=v"(d) : "v"(w));
+}
+
+// a - (fp16 low half of h) and b - (fp16 high half of h), in fp32 (exact
+// when h holds a and b truncated to fp16)
+__device__ __forceinline__ void mix_sub(uint32_t h, float a, float b, float& ra, float& rb) {
+  asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[0,0,0] op_sel_hi:[1,0,0]" : "=v"(ra) : "v"(h), "v"(a));
+  asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(rb) : "v"(h), "v"(b));
+}
+
+// hi/lo fp16 split of a pair: hi = (a, b) rounded toward zero, lo = rest
+__device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+  float ra, rb;
+  mix_sub(hi, a, b, ra, rb);
+  lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(ra, rb));
+}
+
 template <int D, int CB, bool PROD, typename T, bool ROPE>
 __global__ __launch_bounds__(kEncWaves * kWave) void encode_kernel(EncodeParams p) {
   constexpr int NLEV = 1 << CB;
@@ -58,29 +101,48 @@ __global__ __launch_bounds__(kEncWaves * kWave) void encode_kernel(EncodeParams 
   constexpr int W = D * CB / 32;          // code words per row
   constexpr int ROW_BYTES = D * CB / 8;
   constexpr int ALIGN = ROW_BYTES % 16 == 0 ? 16 : (ROW_BYTES % 8 == 0 ? 8 : 4);
+  constexpr bool USE_LUT = CB >= 3;
+  constexpr bool F16 = sizeof(T) == 2 && !ROPE;
   using G = ProdGeom<D>;
 
   __shared__ float s_cent[16];
+  __shared__ float2 s_lut[USE_LUT ? kLutMax : 1];
   __shared__ double s_theta[ROPE ? D / 2 : 1];
   __shared__ uint4 s_frag[PROD ? G::FRAGS * 2 * kWave : 1];
 
   const int tid = threadIdx.x;
+  const EncodeParams* kp = (const EncodeParams*)__builtin_amdgcn_kernarg_segment_ptr();
+  const float cscale = PROD ? 256.f : 1.f;
+  if (tid < 16) s_cent[tid] = kp->codec.centroids[tid] * cscale;
+  if (ROPE && tid < D / 2) s_theta[tid] = kp->theta[tid];
+  if constexpr (USE_LUT) {
+    // grid cell g: (threshold inside the cell or +inf, thresholds below the
+    // cell)
+    const float a = p.lut_a, b = p.lut_b;
+    for (int g = tid; g < p.lut_g; g += blockDim.x) {
+      int base = 0;
+      float thr = INFINITY;
 #pragma unroll
-  for (int k = 0; k < 16; ++k)
-    if (tid == k) s_cent[k] = p.codec.centroids[k];
-  if constexpr (ROPE) {
-#pragma unroll
-    for (int k = 0; k < D / 2; ++k)
-      if (tid == k) s_theta[k] = p.theta[k];
+      for (int k = 0; k < NTH; ++k) {
+        const float tu = fmaf(kp->codec.thresholds[k], a, b);
+        const int cell = (int)tu;
+        base += cell < g ? 1 : 0;
+        if (cell == g) thr = tu;
+      }
+      s_lut[g] = make_float2(thr, __int_as_float(base));
+    }
   }
 
   if constexpr (PROD) {
     // S_hi / S_lo as MFMA A fragments: fragment (mt, ks), lane l holds
-    // S[32 mt + l%32][16 ks + 8 (l/32) + j], j = 0..7.
+    // S[32 mt + perm(l%32)][16 ks + 8 (l/32) + j], j = 0..7, where perm
+    // sends the C row 8 (v/4) + 4 h + v%4 of register v in lane half h to
+    // row 16 h + v.
     for (int t = tid; t < G::FRAGS * kWave; t += blockDim.x) {
       const int lane = t & 63, f = t >> 6;
       const int mt = f / G::KS, ks = f % G::KS;
-      const int m = 32 * mt + (lane & 31);
+      const int rho = lane & 31;
+      const int m = 32 * mt + 16 * ((rho >> 2) & 1) + 4 * (rho >> 3) + (rho & 3);
       const int k0 = 16 * ks + 8 * (lane >> 5);
       const float* srow = p.codec.S + (size_t)m * D + k0;
       const float4 s0 = reinterpret_cast<const float4*>(srow)[0];
@@ -104,71 +166,139 @@ __global__ __launch_bounds__(kEncWaves * kWave) void encode_kernel(EncodeParams 
   const int lane = tid & 63;
   const int64_t ntiles = (p.n_rows + kWave - 1) / kWave;
   const T* __restrict__ xin = reinterpret_cast<const T*>(p.x);
+  const float lut_a = p.lut_a, lut_b = p.lut_b;
 
   for (int64_t tile = (int64_t)blockIdx.x * kEncWaves + wave; tile < ntiles;
        tile += (int64_t)gridDim.x * kEncWaves) {
     const int64_t row = tile * kWave + lane;
     const bool valid = row < p.n_rows;
     float x[D];
-    if (valid) {
-      load_row<D, T>(xin + row * D, x);
-    } else {
+    float nu_s, pre_inv = 1.f;
+    if constexpr (F16) {
+      uint32_t u[D / 2];
+      if (valid) {
 #pragma unroll
-      for (int i = 0; i < D; ++i) x[i] = 0.f;
-    }
-    if constexpr (ROPE) rope_inplace<D>(x, row % p.seq_len, s_theta);
-
-    // nu = |x|.  When the squares leave the normal fp32 range (only fp32
-    // inputs get there) the vector is first scaled exactly by the power of
-    // two that brings its largest entry into [0.5, 1).
-    float nu2 = sum_squares<D>(x);
-    float pre_inv = 1.f;
-    if (!(nu2 >= 0x1p-100f && nu2 <= 0x1p100f)) {
-      float mx = 0.f;
+        for (int j = 0; j < D / 8; ++j) {
+          const uint4 v = reinterpret_cast<const uint4*>(xin + row * D)[j];
+          u[4 * j] = v.x; u[4 * j + 1] = v.y; u[4 * j + 2] = v.z; u[4 * j + 3] = v.w;
+        }
+      } else {
 #pragma unroll
-      for (int i = 0; i < D; ++i) mx = fmaxf(mx, fabsf(x[i]));
-      if (mx > 0.f && mx <= 3.4e38f) {
-        int e;
-        frexpf(mx, &e);
-        const float sc = ldexpf(1.f, -e);
-        pre_inv = ldexpf(1.f, e);
-#pragma unroll
-        for (int i = 0; i < D; ++i) x[i] *= sc;
-        nu2 = sum_squares<D>(x);
+        for (int j = 0; j < D / 2; ++j) u[j] = 0u;
       }
+      typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+      float acc[16];
+#pragma unroll
+      for (int a = 0; a < 16; ++a) acc[a] = 0.f;
+#pragma unroll
+      for (int j = 0; j < D / 2; ++j) {
+        const h2_t hv = __builtin_bit_cast(h2_t, u[j]);
+        acc[j & 15] = __builtin_amdgcn_fdot2(hv, hv, acc[j & 15], false);
+      }
+#pragma unroll
+      for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+        for (int a = 0; a < w; ++a) acc[a] += acc[a + w];
+      // a non-finite input encodes as the zero vector (its norm stays non-finite)
+      if (!(acc[0] <= 3.0e38f)) {
+#pragma unroll
+        for (int j = 0; j < D / 2; ++j) u[j] = 0u;
+      }
+      nu_s = sqrtf(acc[0]);
+#pragma unroll
+      for (int j = 0; j < D / 2; ++j) mix_butterfly(u[j] ^ kp->hflip[j], x[2 * j], x[2 * j + 1]);
+#pragma unroll
+      for (int h = 2; h < D; h <<= 1) {
+#pragma unroll
+        for (int i = 0; i < D; ++i) {
+          if ((i & h) == 0) {
+            const float a = x[i], b = x[i + h];
+            x[i] = a + b;
+            x[i + h] = a - b;
+          }
+        }
+      }
+    } else {
+      if (valid) {
+        load_row<D, T>(xin + row * D, x);
+      } else {
+#pragma unroll
+        for (int i = 0; i < D; ++i) x[i] = 0.f;
+      }
+      if constexpr (ROPE) rope_inplace<D>(x, row % p.seq_len, s_theta);
+      // nu = |x|.  When the squares leave the normal fp32 range (only fp32
+      // inputs get there) the vector is first scaled exactly by the power of
+      // two that brings its largest entry into [0.5, 1).
+      float nu2 = sum_squares<D>(x);
+      if (!(nu2 >= 0x1p-100f && nu2 <= 0x1p100f)) {
+        float mx = 0.f;
+#pragma unroll
+        for (int i = 0; i < D; ++i) mx = fmaxf(mx, fabsf(x[i]));
+        if (mx > 0.f && mx <= 3.4e38f) {
+          int e;
+          frexpf(mx, &e);
+          const float sc = ldexpf(1.f, -e);
+          pre_inv = ldexpf(1.f, e);
+#pragma unroll
+          for (int i = 0; i < D; ++i) x[i] *= sc;
+          nu2 = sum_squares<D>(x);
+        } else if (!(mx <= 3.4e38f)) {
+          // a non-finite input encodes as the zero vector
+#pragma unroll
+          for (int i = 0; i < D; ++i) x[i] = 0.f;
+        }
+      }
+      nu_s = sqrtf(nu2);
+      flip_signs<D>(x, p.codec.flip);
+      wht_inreg<D>(x);
     }
-    const float nu_s = sqrtf(nu2);
     const float nu = nu_s * pre_inv;
+    const bool live = nu_s > 0.f && nu_s <= 3.0e38f;
+    // z = y * inv;  prod residual r' = 256 z - c'
+    const float inv = live ? 1.0f / (sqrtf((float)D) * nu_s) : 0.f;
+    const float inv_p = inv * cscale;
+    const float ua = lut_a * inv;
 
-    flip_signs<D>(x, p.codec.flip);
-    wht_inreg<D>(x);
-    const float inv = nu_s > 0.f ? 1.0f / (sqrtf((float)D) * nu_s) : 0.f;
-
-    // quantize and pack; x keeps z for the residual
+    // the quantizer starts once the butterflies are done (interleaving the
+    // two only raises the register pressure)
+    __builtin_amdgcn_sched_barrier(0);
     uint32_t words[W];
 #pragma unroll
     for (int j = 0; j < W; ++j) words[j] = 0u;
+    // code of coordinate i (packed into words); prod: returns r'_i
+    auto quantize = [&](int i) -> float {
+      int c;
+      float r = 0.f;
+      if constexpr (USE_LUT) {
+        const float u = fmaf(x[i], ua, lut_b);
+        const float2 e = s_lut[(uint32_t)u];
+        c = __float_as_int(e.y) + (u >= e.x ? 1 : 0);
+        if constexpr (PROD) r = fmaf(x[i], inv_p, -s_cent[c]);
+      } else {
+        const float z = x[i] * inv_p;
+        c = 0;
 #pragma unroll
-    for (int i = 0; i < D; ++i) {
-      const float z = x[i] * inv;
-      int c = 0;
-#pragma unroll
-      for (int k = 0; k < NTH; ++k) c += (z >= p.codec.thresholds[k]) ? 1 : 0;
+        for (int k = 0; k < NTH; ++k) c += (z >= p.codec.thresholds[k] * cscale) ? 1 : 0;
+        if constexpr (PROD) r = z - s_cent[c];
+      }
       const int off = i * CB;
       words[off >> 5] |= (uint32_t)c << (off & 31);
       if ((off & 31) + CB > 32) words[(off >> 5) + 1] |= (uint32_t)c >> (32 - (off & 31));
-      x[i] = z;
-    }
-    if (valid) {
-      store_words<W, ALIGN>(p.idx + row * ROW_BYTES, words);
-      p.norm[row] = nu;
-    }
+      return r;
+    };
 
-    if constexpr (PROD) {
-      // Residual r = z - c[idx] and, 16 coordinates at a time, the B
-      // fragments: X = r[16ks .. 16ks+7], Y = r[16ks+8 .. 16ks+15] (scaled by
-      // 2^8, split hi/lo); after the half-wave swap X holds block 0 (tokens
-      // of lanes 0..31) and Y block 1 (tokens of lanes 32..63).
+    if constexpr (!PROD) {
+#pragma unroll
+      for (int i = 0; i < D; ++i) quantize(i);
+      if (valid) {
+        store_words<W, ALIGN>(p.idx + row * ROW_BYTES, words);
+        p.norm[row] = nu;
+      }
+    } else {
+      // 16 coordinates at a time: codes, r' = 256 (z - c[idx]), gamma^2, and
+      // the B fragments: X = r'[16ks .. 16ks+7], Y = r'[16ks+8 .. 16ks+15],
+      // split hi/lo; after the half-wave swap X holds block 0 (tokens of
+      // lanes 0..31) and Y block 1.
       uint32_t b0h[G::KS][4], b1h[G::KS][4], b0l[G::KS][4], b1l[G::KS][4];
       float g2[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -176,29 +306,33 @@ __global__ __launch_bounds__(kEncWaves * kWave) void encode_kernel(EncodeParams 
         float r[16];
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int i = 16 * ks + e;
-          r[e] = x[i] - s_cent[get_code<CB, W>(words, i)];
+          r[e] = quantize(16 * ks + e);
           g2[e & 3] = fmaf(r[e], r[e], g2[e & 3]);
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float xa = r[2 * j] * 256.f, xb = r[2 * j + 1] * 256.f;
-          const float ya = r[8 + 2 * j] * 256.f, yb = r[8 + 2 * j + 1] * 256.f;
-          const _Float16 xah = (_Float16)xa, xbh = (_Float16)xb, yah = (_Float16)ya, ybh = (_Float16)yb;
-          uint32_t xh = pack_h2(xah, xbh), yh = pack_h2(yah, ybh);
-          uint32_t xl = pack_h2((_Float16)(xa - (float)xah), (_Float16)(xb - (float)xbh));
-          uint32_t yl = pack_h2((_Float16)(ya - (float)yah), (_Float16)(yb - (float)ybh));
+          uint32_t xh, xl, yh, yl;
+          split_pair(r[2 * j], r[2 * j + 1], xh, xl);
+          split_pair(r[8 + 2 * j], r[8 + 2 * j + 1], yh, yl);
           swap_halves(xh, yh);
           swap_halves(xl, yl);
           b0h[ks][j] = xh; b1h[ks][j] = yh;
           b0l[ks][j] = xl; b1l[ks][j] = yl;
         }
+        // pin the code words here: left alone, the compiler sinks their
+        // assembly to the store and keeps every compare mask alive until then
+#pragma unroll
+        for (int j = 0; j < W; ++j) asm volatile("" : "+v"(words[j]));
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (valid) p.rnorm[row] = sqrtf((g2[0] + g2[1]) + (g2[2] + g2[3]));
+      if (valid) {
+        store_words<W, ALIGN>(p.idx + row * ROW_BYTES, words);
+        p.norm[row] = nu;
+      }
+      if (valid) p.rnorm[row] = sqrtf((g2[0] + g2[1]) + (g2[2] + g2[3])) * (1.f / 256.f);
 
       uint32_t sign_words[4] = {0u, 0u, 0u, 0u};
-      const uint32_t half_shift = 4u * (uint32_t)(lane >> 5);
+      const uint32_t half_shift = 16u * (uint32_t)(lane >> 5);
       // one 32-row tile of S at a time (not unrolled: bounds the live
       // registers to the B fragments, one tile's A fragments and 32 sums)
 #pragma unroll 1
@@ -224,16 +358,17 @@ __global__ __launch_bounds__(kEncWaves * kWave) void encode_kernel(EncodeParams 
           // live registers to one step's operands
           __builtin_amdgcn_sched_barrier(0);
         }
-        // C layout: lane l holds column l%32, rows 8 (v/4) + 4 (l/32) + v%4
+        // register v of lane half h holds row 16 h + v of the tile: shift the
+        // sign bits in from v = 15 down to 0, then bit = [p >= 0] (a result
+        // of exactly -0 reads as negative; it needs r = 0)
         uint32_t w0 = 0u, w1 = 0u;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int pos = 8 * (v >> 2) + (v & 3);
-          w0 |= (c0[v] >= 0.f ? 1u : 0u) << pos;
-          w1 |= (c1[v] >= 0.f ? 1u : 0u) << pos;
+        for (int v = 15; v >= 0; --v) {
+          w0 = __builtin_amdgcn_alignbit(w0, __float_as_uint(c0[v]), 31);
+          w1 = __builtin_amdgcn_alignbit(w1, __float_as_uint(c1[v]), 31);
         }
-        w0 <<= half_shift;
-        w1 <<= half_shift;
+        w0 = (w0 ^ 0xFFFFu) << half_shift;
+        w1 = (w1 ^ 0xFFFFu) << half_shift;
         swap_halves(w0, w1);
         const uint32_t word = w0 | w1;
         sign_words[0] = mt == 0 ? word : sign_words[0];
@@ -250,6 +385,360 @@ __global__ __launch_bounds__(kEncWaves * kWave) void encode_kernel(EncodeParams 
       }
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// fp16 input without RoPE: two lanes per vector.  Lane l of a wave owns
+// token 32 tile + l%32 and the coordinate half h = l/32 (coordinates
+// h d/2 .. h d/2 + d/2 - 1), which halves the registers a vector needs and
+// lets more waves hide the HBM latency.  The butterfly stages commute; the
+// one across the halves (coordinate bit log2(d/2)) runs first, on the
+// packed fp16 input: one v_permlane32_swap gives every lane both halves'
+// pair, and v_fma_mix_f32 forms x_low + x_high (low lane) or
+// x_low - x_high (high lane) in fp32.  The other stages stay in registers.
+// For prod, the B operand of the projection takes, in lane l at k step ks,
+// the lane's own residuals 8 ks .. 8 ks + 7 (k slot j of lane half h is
+// coordinate h d/2 + 8 ks + j; the A fragments of S use the same order),
+// so no exchange is needed, and both lane halves hold 16 of the 32 sign
+// bits of each 32-row tile.
+
+// Workgroup shape.  prod: the 64 KB of S fragments allow two workgroups
+// per CU; eight waves each at two waves per SIMD leave the registers for
+// loading the next tile's input while the current one is processed.  mse:
+// small workgroups at four waves per SIMD (a prefetch measured no faster).
+template <bool PROD>
+struct HalfLaunch {
+  static constexpr bool kPrefetch = PROD;
+  static constexpr int kWaves = PROD ? 8 : 4;
+  static constexpr int kMinWavesPerEU = PROD ? 2 : 4;
+};
+
+// v from the low half plus v from the high half, in every lane
+__device__ __forceinline__ float cross_sum(float v) {
+  uint32_t a = __float_as_uint(v), b = a;
+  swap_halves(a, b);
+  return __uint_as_float(a) + __uint_as_float(b);
+}
+
+template <int D, int CB, bool PROD>
+__global__ __launch_bounds__(HalfLaunch<PROD>::kWaves * kWave, HalfLaunch<PROD>::kMinWavesPerEU) void encode_half_kernel(EncodeParams p) {
+  constexpr int kHalfWaves = HalfLaunch<PROD>::kWaves;
+  constexpr int NLEV = 1 << CB;
+  constexpr int NTH = NLEV - 1;
+  constexpr int HALF = D / 2;              // coordinates per lane
+  constexpr int NP = D / 4;                // packed fp16 pairs per lane
+  constexpr int HW = HALF * CB / 32;       // code words per lane (half a row)
+  constexpr int ROW_BYTES = D * CB / 8;
+  constexpr int HB = ROW_BYTES / 2;
+  constexpr int HALIGN = HB % 16 == 0 ? 16 : (HB % 8 == 0 ? 8 : 4);
+  constexpr bool USE_LUT = CB >= 3;
+  constexpr int KS = D / 16, MT = D / 32, FRAGS = MT * KS;
+
+  __shared__ float s_cent[16];
+  __shared__ float2 s_lut[USE_LUT ? kLutMax : 1];
+  __shared__ uint4 s_hmask[NP / 2];
+  __shared__ uint4 s_frag[PROD ? FRAGS * 2 * kWave : 1];
+
+  const int tid = threadIdx.x;
+  const EncodeParams* kp = (const EncodeParams*)__builtin_amdgcn_kernarg_segment_ptr();
+  const float cscale = PROD ? 256.f : 1.f;
+  if (tid < 16) s_cent[tid] = kp->codec.centroids[tid] * cscale;
+  if (tid >= 64 && tid < 64 + NP / 2)
+    s_hmask[tid - 64] = make_uint4(kp->hflip[4 * (tid - 64)], kp->hflip[4 * (tid - 64) + 1],
+                                   kp->hflip[4 * (tid - 64) + 2], kp->hflip[4 * (tid - 64) + 3]);
+  if constexpr (USE_LUT) {
+    const float a = p.lut_a, b = p.lut_b;
+    for (int g = tid; g < p.lut_g; g += blockDim.x) {
+      int base = 0;
+      float thr = INFINITY;
+#pragma unroll
+      for (int k = 0; k < NTH; ++k) {
+        const float tu = fmaf(kp->codec.thresholds[k], a, b);
+        const int cell = (int)tu;
+        base += cell < g ? 1 : 0;
+        if (cell == g) thr = tu;
+      }
+      s_lut[g] = make_float2(thr, __int_as_float(base));
+    }
+  }
+  if constexpr (PROD) {
+    // fragment (mt, ks), lane l: row 32 mt + perm(l%32) of S (perm as in the
+    // one-vector-per-lane kernel), columns (l/32) d/2 + 8 ks + 0..7
+    for (int t = tid; t < FRAGS * kWave; t += blockDim.x) {
+      const int lane = t & 63, f = t >> 6;
+      const int mt = f / KS, ks = f % KS;
+      const int rho = lane & 31;
+      const int m = 32 * mt + 16 * ((rho >> 2) & 1) + 4 * (rho >> 3) + (rho & 3);
+      const int k0 = (lane >> 5) * HALF + 8 * ks;
+      const float* srow = p.codec.S + (size_t)m * D + k0;
+      const float4 s0 = reinterpret_cast<const float4*>(srow)[0];
+      const float4 s1 = reinterpret_cast<const float4*>(srow)[1];
+      const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+      _Float16 hi[8], lo[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        hi[j] = (_Float16)sv[j];
+        lo[j] = (_Float16)(sv[j] - (float)hi[j]);
+      }
+      s_frag[(2 * f) * kWave + lane] =
+          make_uint4(pack_h2(hi[0], hi[1]), pack_h2(hi[2], hi[3]), pack_h2(hi[4], hi[5]), pack_h2(hi[6], hi[7]));
+      s_frag[(2 * f + 1) * kWave + lane] =
+          make_uint4(pack_h2(lo[0], lo[1]), pack_h2(lo[2], lo[3]), pack_h2(lo[4], lo[5]), pack_h2(lo[6], lo[7]));
+    }
+  }
+  __syncthreads();
+
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int h = lane >> 5;
+  const float sgn = h ? -1.f : 1.f;
+  const int64_t ntiles = (p.n_rows + 31) / 32;
+  const _Float16* __restrict__ xin = reinterpret_cast<const _Float16*>(p.x);
+  const float lut_a = p.lut_a, lut_b = p.lut_b;
+
+  // the input of the wave's next tile is loaded while the current one is
+  // processed (rows past the end read as zeros and are not stored)
+  auto load_tile = [&](int64_t t, uint32_t (&dst)[NP]) {
+    const int64_t r = t * 32 + (lane & 31);
+    if (t < ntiles && r < p.n_rows) {
+      const uint4* src = reinterpret_cast<const uint4*>(xin + r * D + h * HALF);
+#pragma unroll
+      for (int j = 0; j < NP / 4; ++j) {
+        const uint4 v = src[j];
+        dst[4 * j] = v.x; dst[4 * j + 1] = v.y; dst[4 * j + 2] = v.z; dst[4 * j + 3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NP; ++j) dst[j] = 0u;
+    }
+  };
+  const int64_t tstride = (int64_t)gridDim.x * kHalfWaves;
+  int64_t tile = (int64_t)blockIdx.x * kHalfWaves + wave;
+  constexpr bool PF = HalfLaunch<PROD>::kPrefetch;
+  uint32_t nxt[NP];
+  if (PF) load_tile(tile, nxt);
+  for (; tile < ntiles; tile += tstride) {
+    const int64_t row = tile * 32 + (lane & 31);
+    const bool valid = row < p.n_rows;
+    uint32_t u[NP];
+    if (PF) {
+#pragma unroll
+      for (int j = 0; j < NP; ++j) u[j] = nxt[j];
+    } else if (valid) {
+      const uint4* src = reinterpret_cast<const uint4*>(xin + row * D + h * HALF);
+#pragma unroll
+      for (int j = 0; j < NP / 4; ++j) {
+        const uint4 v = src[j];
+        u[4 * j] = v.x; u[4 * j + 1] = v.y; u[4 * j + 2] = v.z; u[4 * j + 3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NP; ++j) u[j] = 0u;
+    }
+    typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+    float acc[8];
+#pragma unroll
+    for (int a = 0; a < 8; ++a) acc[a] = 0.f;
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      const h2_t hv = __builtin_bit_cast(h2_t, u[j]);
+      acc[j & 7] = __builtin_amdgcn_fdot2(hv, hv, acc[j & 7], false);
+    }
+#pragma unroll
+    for (int w = 4; w >= 1; w >>= 1)
+#pragma unroll
+      for (int a = 0; a < w; ++a) acc[a] += acc[a + w];
+    const float nu2 = cross_sum(acc[0]);
+    // a non-finite input encodes as the zero vector (its norm stays non-finite)
+    if (!(nu2 <= 3.0e38f)) {
+#pragma unroll
+      for (int j = 0; j < NP; ++j) u[j] = 0u;
+    }
+    const float nu_s = sqrtf(nu2);
+
+    // sign flip, the stage across the halves, and the stage on bit 0
+    float x[HALF];
+#pragma unroll
+    for (int j4 = 0; j4 < NP / 4; ++j4) {
+      const uint4 m4 = s_hmask[h * (NP / 4) + j4];
+      const uint32_t ms[4] = {m4.x, m4.y, m4.z, m4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = 4 * j4 + e;
+        uint32_t a = u[j] ^ ms[e], b = a;
+        swap_halves(a, b);   // a: the low lane's pair, b: the high lane's pair
+        float t0, t1;
+        asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,0,0] op_sel_hi:[1,0,1]" : "=v"(t0) : "v"(b), "v"(sgn), "v"(a));
+        asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,1] op_sel_hi:[1,0,1]" : "=v"(t1) : "v"(b), "v"(sgn), "v"(a));
+        x[2 * j] = t0 + t1;
+        x[2 * j + 1] = t0 - t1;
+      }
+    }
+    if (PF) load_tile(tile + tstride, nxt);
+#pragma unroll
+    for (int hh = 2; hh < HALF; hh <<= 1) {
+#pragma unroll
+      for (int i = 0; i < HALF; ++i) {
+        if ((i & hh) == 0) {
+          const float a = x[i], b = x[i + hh];
+          x[i] = a + b;
+          x[i + hh] = a - b;
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    const bool live = nu_s > 0.f && nu_s <= 3.0e38f;
+    const float inv = live ? 1.0f / (sqrtf((float)D) * nu_s) : 0.f;
+    const float inv_p = inv * cscale;
+    const float ua = lut_a * inv;
+    uint32_t words[HW];
+#pragma unroll
+    for (int j = 0; j < HW; ++j) words[j] = 0u;
+    auto quantize = [&](int i) -> float {
+      int c;
+      float r = 0.f;
+      if constexpr (USE_LUT) {
+        const float uu = fmaf(x[i], ua, lut_b);
+        const float2 e = s_lut[(uint32_t)uu];
+        c = __float_as_int(e.y) + (uu >= e.x ? 1 : 0);
+        if constexpr (PROD) r = fmaf(x[i], inv_p, -s_cent[c]);
+      } else {
+        const float z = x[i] * inv_p;
+        c = 0;
+#pragma unroll
+        for (int k = 0; k < NTH; ++k) c += (z >= p.codec.thresholds[k] * cscale) ? 1 : 0;
+        if constexpr (PROD) r = z - s_cent[c];
+      }
+      const int off = i * CB;
+      words[off >> 5] |= (uint32_t)c << (off & 31);
+      if ((off & 31) + CB > 32) words[(off >> 5) + 1] |= (uint32_t)c >> (32 - (off & 31));
+      return r;
+    };
+    uint8_t* idx_dst = p.idx + row * ROW_BYTES + h * HB;
+
+    if constexpr (!PROD) {
+#pragma unroll
+      for (int i = 0; i < HALF; ++i) quantize(i);
+      if (valid) {
+        store_words<HW, HALIGN>(idx_dst, words);
+        if (h == 0) p.norm[row] = nu_s;
+      }
+    } else {
+      uint32_t bh[KS][4], bl[KS][4];
+      float g2[2] = {0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        float r[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          r[e] = quantize(8 * ks + e);
+          g2[e & 1] = fmaf(r[e], r[e], g2[e & 1]);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) split_pair(r[2 * j], r[2 * j + 1], bh[ks][j], bl[ks][j]);
+        // pin the code words and the packed fragments here: left alone, the
+        // compiler sinks their assembly to the first use and keeps the
+        // compare masks and unpacked fp32 parts alive until then
+#pragma unroll
+        for (int j = 0; j < HW; ++j) asm volatile("" : "+v"(words[j]));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(bh[ks][j]), "+v"(bl[ks][j]));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (valid) {
+        store_words<HW, HALIGN>(idx_dst, words);
+        if (h == 0) p.norm[row] = nu_s;
+      }
+      const float gamma2 = cross_sum(g2[0] + g2[1]);
+      if (valid && h == 0) p.rnorm[row] = sqrtf(gamma2) * (1.f / 256.f);
+
+      // S r' on the matrix cores, two 32-row tiles of S at a time
+      uint32_t sw[MT];
+#pragma unroll 1
+      for (int mp = 0; mp < MT / 2; ++mp) {
+        f32x16 c0 = {}, c1 = {};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const int f0 = (2 * mp) * KS + ks, f1 = (2 * mp + 1) * KS + ks;
+          const half8_t a0h = __builtin_bit_cast(half8_t, s_frag[(2 * f0) * kWave + lane]);
+          const half8_t a0l = __builtin_bit_cast(half8_t, s_frag[(2 * f0 + 1) * kWave + lane]);
+          const half8_t a1h = __builtin_bit_cast(half8_t, s_frag[(2 * f1) * kWave + lane]);
+          const half8_t a1l = __builtin_bit_cast(half8_t, s_frag[(2 * f1 + 1) * kWave + lane]);
+          const half8_t rh = __builtin_bit_cast(half8_t, make_uint4(bh[ks][0], bh[ks][1], bh[ks][2], bh[ks][3]));
+          const half8_t rl = __builtin_bit_cast(half8_t, make_uint4(bl[ks][0], bl[ks][1], bl[ks][2], bl[ks][3]));
+          c0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0h, rh, c0, 0, 0, 0);
+          c1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1h, rh, c1, 0, 0, 0);
+          c0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0h, rl, c0, 0, 0, 0);
+          c1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1h, rl, c1, 0, 0, 0);
+          c0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0l, rh, c0, 0, 0, 0);
+          c1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1l, rh, c1, 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // register v of lane half h holds row 16 h + v of the tile; bit =
+        // [p >= 0] (a result of exactly -0 reads as negative; it needs r = 0)
+        uint32_t w0 = 0u, w1 = 0u;
+#pragma unroll
+        for (int v = 15; v >= 0; --v) {
+          w0 = __builtin_amdgcn_alignbit(w0, __float_as_uint(c0[v]), 31);
+          w1 = __builtin_amdgcn_alignbit(w1, __float_as_uint(c1[v]), 31);
+        }
+        w0 = (w0 ^ 0xFFFFu) << (16 * h);
+        w1 = (w1 ^ 0xFFFFu) << (16 * h);
+        uint32_t a0 = w0, b0 = w0, a1 = w1, b1 = w1;
+        swap_halves(a0, b0);
+        swap_halves(a1, b1);
+#pragma unroll
+        for (int t = 0; t < MT / 2; ++t) {
+          if (t == mp) {
+            sw[2 * t] = a0 | b0;
+            sw[2 * t + 1] = a1 | b1;
+          }
+        }
+      }
+      // lane half h stores words h MT/2 .. h MT/2 + MT/2 - 1
+      if (valid) {
+        uint32_t* qdst = reinterpret_cast<uint32_t*>(p.qjl + row * (D / 8)) + h * (MT / 2);
+        if constexpr (MT == 4) {
+          *reinterpret_cast<uint2*>(qdst) = make_uint2(h ? sw[2] : sw[0], h ? sw[3] : sw[1]);
+        } else {
+          *qdst = h ? sw[1] : sw[0];
+        }
+      }
+    }
+  }
+}
+
+template <int D, int CB, bool PROD>
+static hipError_t run_half(const EncodeParams& p, hipStream_t stream) {
+  constexpr int kHalfWaves = HalfLaunch<PROD>::kWaves;
+  static int per_cu = 0;
+  if (per_cu == 0) {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, encode_half_kernel<D, CB, PROD>,
+                                                     kHalfWaves * kWave, 0) != hipSuccess || nb < 1)
+      nb = 1;
+    per_cu = nb;
+  }
+  const int64_t ntiles = (p.n_rows + 31) / 32;
+  int64_t blocks = (ntiles + kHalfWaves - 1) / kHalfWaves;
+  const int64_t cap = (int64_t)device_cu_count() * per_cu;
+  if (blocks > cap) blocks = cap;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL((encode_half_kernel<D, CB, PROD>), dim3((unsigned)blocks),
+                     dim3(kHalfWaves * kWave), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int D, bool PROD>
+static hipError_t pick_half(int cb, const EncodeParams& p, hipStream_t s) {
+  switch (cb) {
+    case 1: return run_half<D, 1, PROD>(p, s);
+    case 2: return run_half<D, 2, PROD>(p, s);
+    case 3: return run_half<D, 3, PROD>(p, s);
+    case 4: return run_half<D, 4, PROD>(p, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int D, int CB, bool PROD, typename T, bool ROPE>
@@ -289,8 +778,34 @@ static hipError_t pick_rest(const tq_codec& c, int dtype, bool rope, const Encod
                   : pick_cb<D, false, _Float16, true>(c.code_bits, p, s);
     return hipErrorInvalidValue;
   }
-  return prod ? pick_cb<D, true, _Float16, false>(c.code_bits, p, s)
-              : pick_cb<D, false, _Float16, false>(c.code_bits, p, s);
+  return prod ? pick_half<D, true>(c.code_bits, p, s) : pick_half<D, false>(c.code_bits, p, s);
+}
+
+// Smallest grid (G cells over z in [-1.01, 1.01], one cell of margin on
+// each side) in which no two thresholds share a cell, with the cell of a
+// threshold computed exactly as the kernel computes it.
+static bool build_grid(const tq_codec& c, EncodeParams& p) {
+  const int nth = (1 << c.code_bits) - 1;
+  for (int G = 32; G <= kLutMax; G *= 2) {
+    const float a = (float)((G / 2 - 1) / (double)kGridRange);
+    const float b = (float)(G / 2);
+    bool ok = true;
+    int prev = -1;
+    for (int k = 0; k < nth && ok; ++k) {
+      const float tu = std::fmaf(c.thresholds[k], a, b);
+      if (!(tu >= 0.f && tu < (float)G)) { ok = false; break; }
+      const int cell = (int)tu;
+      if (cell <= prev) ok = false;
+      prev = cell;
+    }
+    if (ok) {
+      p.lut_g = G;
+      p.lut_a = a;
+      p.lut_b = b;
+      return true;
+    }
+  }
+  return false;
 }
 
 hipError_t launch_encode(const tq_codec& c, const void* x, int dtype, int64_t n_rows,
@@ -308,6 +823,11 @@ hipError_t launch_encode(const tq_codec& c, const void* x, int dtype, int64_t n_
     p.codec.thresholds[k] = c.thresholds[k];
   }
   for (int w = 0; w < 48; ++w) p.codec.flip[w] = c.flip[w];
+  for (int j = 0; j < 64 && 2 * j + 1 < c.d; ++j) {
+    const uint32_t b0 = (c.flip[(2 * j) >> 5] >> ((2 * j) & 31)) & 1u;
+    const uint32_t b1 = (c.flip[(2 * j + 1) >> 5] >> ((2 * j + 1) & 31)) & 1u;
+    p.hflip[j] = (b0 << 15) | (b1 << 31);
+  }
   p.codec.S = c.S;
   p.codec.d = c.d;
   p.codec.code_bits = c.code_bits;
@@ -318,6 +838,7 @@ hipError_t launch_encode(const tq_codec& c, const void* x, int dtype, int64_t n_
     for (int i = 0; i < c.d / 2 && i < 64; ++i)
       p.theta[i] = std::pow((double)rope.base, -2.0 * i / (double)c.d);
   }
+  if (c.code_bits >= 3 && !build_grid(c, p)) return hipErrorInvalidValue;
   if (c.d == 128) return pick_rest<128>(c, dtype, rope.on, p, stream);
   if (c.d == 64) return pick_rest<64>(c, dtype, rope.on, p, stream);
   return hipErrorInvalidValue;

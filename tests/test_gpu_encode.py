@@ -101,6 +101,32 @@ def test_encode_ragged_all_widths(d, mode, bits):
     assert to_np(out.norm)[3] == 0.0
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("mode,bits", [(0, 1), (0, 2), (0, 3), (0, 4), (1, 2), (1, 3), (1, 4), (1, 5)])
+def test_encode_ragged_all_widths_fp16(d, mode, bits):
+    """fp16 input (two lanes per vector on the GPU): every code width, a
+    ragged count that ends inside a 32-token tile, a zero vector and an
+    fp16 subnormal-only vector."""
+    say("encode fp16 ragged d=%d mode=%d bits=%d" % (d, mode, bits))
+    rng = np.random.default_rng(1000 + 100 * d + 10 * mode + bits)
+    n = 32 * 41 + 17
+    x = (rng.standard_normal((n, d)) * rng.uniform(0.1, 10, (n, 1))).astype(np.float16)
+    x[5] = 0.0
+    x[6] = np.float16(3e-6)                       # subnormal fp16 entries
+    draws = synth.codec_draws(rng, d, m=d if mode else 0)
+    codec = make_codec(d, mode, bits, draws)
+    t = torch.from_numpy(x).cuda()
+    if mode == tq.TQ_PROD:
+        out, _ = tq.encode_kv(codec, None, t, None)
+        torch.cuda.synchronize()
+        check_prod(x.astype(np.float64), out, codec, draws)
+    else:
+        _, out = tq.encode_kv(None, codec, None, t)
+        torch.cuda.synchronize()
+        check_mse(x.astype(np.float64), out, codec, draws)
+    assert to_np(out.norm)[5] == 0.0
+
+
 @pytest.mark.parametrize("n", [1, 63, 64, 65, 513])
 def test_encode_small_counts_fp16(n):
     say("encode small n=%d" % n)
