@@ -14,11 +14,13 @@ eight code sets rotate so that each encode reads its input from HBM and each
 attention step reads codes written four steps earlier (more than the 256 MB
 Infinity Cache has passed through since), not from the cache.
 
-Prints one JSON line.  `value` is KV vectors encoded per second over whole
-steps (encode + attention).  The per-kernel rates come from HIP events on
-the stream the kernels run on; `roofline` describes the kernel with the
-largest share of the step.  `cpu_baseline` times the fp64 CPU oracle on a
-bounded sample of the same workload on this host.
+Each step is replayed from a HIP graph captured once per buffer set, so
+that host launch overhead stays out of the timed loop.  Prints one JSON
+line.  `value` is KV vectors encoded per second over whole steps (encode +
+attention).  The per-kernel rates come from HIP events on the replay stream
+around graphs holding one launch per buffer set; `roofline` describes the
+kernel with the largest share of the step.  `cpu_baseline` times the fp64 CPU
+oracle on a bounded sample of the same workload on this host.
 """
 
 import argparse
@@ -30,6 +32,14 @@ import time
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0
+
+# HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE passes of the
+# current kernels, scaled by the runtime copy kernel's reading on a known
+# 64 MiB copy (FETCH_SIZE x2.0, WRITE_SIZE x1.0); None where the kernel has
+# changed since the counters were taken.
+TRAFFIC = {"encode_k": (33138 * 2 + 18432) * 1024,
+           "encode_v": (32852 * 2 + 17410) * 1024,
+           "attend": (18334 * 2 + 520 + 365 * 2 + 16) * 1024}
 
 
 def parse():
@@ -77,36 +87,59 @@ def main():
         tq.encode_kv(kc, vc, ks[i], vs[i], kout=kpk[i], vout=vpk[i])
     torch.cuda.synchronize()
 
-    def step(i, ev=None):
-        j = i % S
-        if ev is not None:
-            ev[0].record()
+    def enc_k(j):
         tq.encode_kv(kc, None, ks[j], None, kout=kpk[j])
-        if ev is not None:
-            ev[1].record()
+
+    def enc_v(j):
         tq.encode_kv(None, vc, None, vs[j], vout=vpk[j])
-        if ev is not None:
-            ev[2].record()
-        r = (i + S // 2) % S
+
+    def attend(j):
+        r = (j + S // 2) % S
         tq.attend_decode(kc, vc, q, kpk[r], vpk[r], ctx, hkv, out=out, workspace=ws)
-        if ev is not None:
-            ev[3].record()
+
+    def step(j):
+        enc_k(j)
+        enc_v(j)
+        attend(j)
 
     for i in range(a.warmup):
-        step(i)
+        step(i % S)
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(a.steps)]
+    # One HIP graph per step (one per buffer set) takes the Python launch
+    # overhead out of the timed loop; the library's launches are captured on
+    # the capture stream like any other work.
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        return g
+
+    g_step = [capture(lambda j=j: step(j)) for j in range(S)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(a.steps):
-        step(a.warmup + i, evs[i])
+        g_step[i % S].replay()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    ek = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3   # seconds
-    ekv = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
-    ea = np.array([e[2].elapsed_time(e[3]) for e in evs]) * 1e-3
+    # Per-kernel durations: HIP events on the capture-and-replay stream around
+    # graphs that hold one launch per buffer set, replayed back to back.
+    g_parts = {name: capture(lambda fn=fn: [fn(j) for j in range(S)])
+               for name, fn in (("encode_k", enc_k), ("encode_v", enc_v), ("attend", attend))}
+    reps = max(2, a.steps // S)
+    t_part = {}
+    for name, g in g_parts.items():
+        g.replay()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        t_part[name] = e0.elapsed_time(e1) * 1e-3 / (reps * S)     # seconds per launch
+
     ms_per_step = wall / a.steps * 1e3
     vectors = 2 * n
 
@@ -115,22 +148,22 @@ def main():
     kbytes = n * (d * 2 + d * 3 // 8 + d // 8 + 8)
     vbytes = n * (d * 2 + d * 4 // 8 + 4)
     abytes = n * ((d * 3 // 8 + d // 8 + 8) + (d * 4 // 8 + 4))
-    tk, tv, ta = float(np.mean(ek)), float(np.mean(ekv)), float(np.mean(ea))
+    tk, tv, ta = t_part["encode_k"], t_part["encode_v"], t_part["attend"]
     enc = {"us_k": tk * 1e6, "us_v": tv * 1e6,
            "vectors_per_s": vectors / (tk + tv),
            "GB_per_s": (kbytes + vbytes) / (tk + tv) / 1e9,
            "frac_of_hbm_peak": (kbytes + vbytes) / (tk + tv) / 1e9 / HBM_PEAK_GBS}
     att = {"us": ta * 1e6, "GB_per_s": abytes / ta / 1e9,
            "frac_of_hbm_peak": abytes / ta / 1e9 / HBM_PEAK_GBS,
-           "note": "includes the query-prep and merge launches of the call"}
+           "note": "one tq_attend_decode call: decode kernel + log-sum-exp merge kernel"}
     parts = {"encode_k": (tk, kbytes), "encode_v": (tv, vbytes), "attend": (ta, abytes)}
     dom = max(parts, key=lambda p: parts[p][0])
     t_dom, b_dom = parts[dom]
-    roof = {"kernel": {"encode_k": "encode_kernel<128,3,prod,fp16>",
-                       "encode_v": "encode_kernel<128,4,mse,fp16>",
-                       "attend": "attend_kernel<128,3,4> (+ qprep, combine)"}[dom],
+    roof = {"kernel": {"encode_k": "encode_half_kernel<128,3,prod> (keys, fp16)",
+                       "encode_v": "encode_half_kernel<128,4,mse> (values, fp16)",
+                       "attend": "decode_kernel<128,3,4> + merge_kernel<128>"}[dom],
             "bound": "hbm", "achieved": b_dom / t_dom / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": b_dom / t_dom / 1e9 / HBM_PEAK_GBS, "traffic": None}
+            "frac": b_dom / t_dom / 1e9 / HBM_PEAK_GBS, "traffic": TRAFFIC.get(dom)}
 
     res = {
         "metric": "KV vectors encoded/s and decode-attention GB/s over packed codes (% of HBM peak)",
@@ -164,15 +197,18 @@ def cpu_baseline(w):
     k = w["k"][:heads].reshape(-1, d).astype(np.float64)
     v = w["v"][:heads].reshape(-1, d).astype(np.float64)
     q = w["q"][:4 * heads].astype(np.float64).reshape(1, 4 * heads, 1, d)
-    t0 = time.perf_counter()
-    ek = oracle.encode_prod(k, flip, kc, kt, S)
-    ev = oracle.encode_mse(v, flip, vt)
-    kcodes = {"idx": ek.idx.reshape(1, heads, ctx, d), "sign": ek.sign.reshape(1, heads, ctx, d),
-              "norm": ek.norm.reshape(1, heads, ctx), "rnorm": ek.rnorm.reshape(1, heads, ctx)}
-    vcodes = {"idx": ev.idx.reshape(1, heads, ctx, d), "norm": ev.norm.reshape(1, heads, ctx)}
-    oracle.attention_from_codes(q, kcodes, vcodes, {"signs": flip, "centroids": kc, "S": S},
-                                {"signs": flip, "centroids": vc})
-    dt = time.perf_counter() - t0
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        ek = oracle.encode_prod(k, flip, kc, kt, S)
+        ev = oracle.encode_mse(v, flip, vt)
+        kcodes = {"idx": ek.idx.reshape(1, heads, ctx, d), "sign": ek.sign.reshape(1, heads, ctx, d),
+                  "norm": ek.norm.reshape(1, heads, ctx), "rnorm": ek.rnorm.reshape(1, heads, ctx)}
+        vcodes = {"idx": ev.idx.reshape(1, heads, ctx, d), "norm": ev.norm.reshape(1, heads, ctx)}
+        oracle.attention_from_codes(q, kcodes, vcodes, {"signs": flip, "centroids": kc, "S": S},
+                                    {"signs": flip, "centroids": vc})
+        times.append(time.perf_counter() - t0)
+    dt = float(np.median(times))
     try:
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
@@ -186,7 +222,7 @@ def cpu_baseline(w):
     return {"value": 2 * heads * ctx / dt, "unit": "vectors/s", "cores": int(threads),
             "kind": "oracle", "seconds": dt,
             "sample": "one full step (%d KV heads): encode of %d keys + %d values and the "
-                      "attention of %d query heads over 32768 tokens (fp64 numpy)" %
+                      "attention of %d query heads over 32768 tokens (fp64 numpy), median of 3" %
                       (heads, heads * ctx, heads * ctx, 4 * heads)}
 
 
