@@ -133,19 +133,28 @@ typedef struct tq_rope {
 
 /* ---- a2..a7: encode --------------------------------------------------------
  * Encodes n_rows rows of K with `kc` into `kout` and n_rows rows of V with
- * `vc` into `vout` in one launch; pass NULL for a side to skip it.  Per row:
+ * `vc` into `vout`; pass NULL for a side to skip it.  Per row:
  * (RoPE on K if `rope` is not NULL), nu = |x|, z = Pi x / nu, idx_i =
  * #{k : z_i >= t_k}, and for TQ_PROD r = z - c[idx], gamma = |r|, signs of
  * S r ("FibQuant" 2.3; "Google presenta TurboQuant" mechanics and prod
- * sections).  The zero vector encodes as z = 0 with nu = 0.
+ * sections).  The zero vector, and a vector with a non-finite element,
+ * encode as z = 0 with nu = 0.
  *   k, v      device, n_rows x d elements of type `dtype`, 16-byte aligned
- *   kc, vc    host structs (kc TQ_PROD or TQ_MSE; vc either)
+ *   kc, vc    host structs (kc TQ_PROD or TQ_MSE; vc either); d = 64, 128 or
+ *             1536 (d = 1536: Pi uses H_12 (x) H_128, H_12 by Paley's
+ *             construction at q = 11; qjl planes 16-byte aligned)
  *   kout/vout host structs of device planes sized for n_rows
- * Returns TQ_OK, TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED or TQ_ERR_HIP. */
+ *   workspace device, >= tq_encode_kv_workspace(kc, vc, n_rows) bytes,
+ *             256-byte aligned; may be NULL when that size is 0 (it is 0
+ *             for d = 64 and 128 and for TQ_MSE).  Contents need no
+ *             initialisation; calls sharing it must not overlap in time.
+ * Returns TQ_OK, TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_WORKSPACE or
+ * TQ_ERR_HIP. */
+size_t tq_encode_kv_workspace(const tq_codec* kc, const tq_codec* vc, int64_t n_rows);
 int tq_encode_kv(const tq_codec* kc, const tq_codec* vc, const void* k,
                  const void* v, int dtype, int64_t n_rows, const tq_rope* rope,
-                 const tq_packed* kout, const tq_packed* vout,
-                 tq_stream_t stream);
+                 const tq_packed* kout, const tq_packed* vout, void* workspace,
+                 size_t workspace_bytes, tq_stream_t stream);
 
 /* ---- a8..a11: attention from codes ----------------------------------------
  * For every batch b, query head h (KV head g = h / (hq / hkv)) and query a:
@@ -155,7 +164,8 @@ int tq_encode_kv(const tq_codec* kc, const tq_codec* vc, const void* k,
  * over all ctx tokens (no causal mask), computed in one pass over the codes
  * with an online softmax split over token ranges and merged by log-sum-exp
  * ("TurboESM" 2E; "Google presenta TurboQuant", unbiased estimator).
- *   kc  TQ_PROD codec of the keys; vc TQ_MSE codec of the values
+ *   kc  TQ_PROD codec of the keys; vc TQ_MSE codec of the values; d = 64 or
+ *       128 (other d: TQ_ERR_UNSUPPORTED)
  *   q   device [batch][hq][n_q][d] of `q_dtype`
  *   k,v host structs of device planes, rows [batch][hkv][ctx]
  *   scale  0 selects 1/sqrt(d)
@@ -178,7 +188,9 @@ int tq_attend_decode(const tq_codec* kc, const tq_codec* vc, const void* q,
  *                    <S Pi q_a, 2 sigma_j - 1> )  (mse: first term only)
  * for n_q queries against n packed rows ("Google presenta TurboQuant",
  * "Velocidad y eficiencia de indexación").
- *   q        device [n_q][d] of `q_dtype`
+ *   q        device [n_q][d] of `q_dtype`; d = 64, 128 or 1536 (at d = 1536
+ *            a 1-bit table must be symmetric, c[0] = -c[1], as
+ *            tq_codec_init builds it)
  *   out      NULL, or device [n_q][n] fp32
  *   top_k    0, or 1..64: per query the top_k largest estimates, descending,
  *            ties to the lower row index, into top_ids [n_q][top_k] (int64)

@@ -22,7 +22,8 @@ TQ_ERR_NOT_CONVERGED, TQ_ERR_HIP, TQ_ERR_WORKSPACE = -3, -4, -5
 TQ_MSE, TQ_PROD = 0, 1
 TQ_F16, TQ_F32 = 0, 1
 
-EXPORTS = ("tq_status_string", "tq_build_codebook", "tq_codec_init", "tq_encode_kv",
+EXPORTS = ("tq_status_string", "tq_build_codebook", "tq_codec_init", "tq_encode_kv_workspace",
+           "tq_encode_kv",
            "tq_attend_decode_workspace", "tq_attend_decode",
            "tq_inner_product_workspace", "tq_inner_product")
 
@@ -68,10 +69,12 @@ def lib():
     L.tq_build_codebook.argtypes = [I, I, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
     L.tq_codec_init.restype = I
     L.tq_codec_init.argtypes = [ctypes.POINTER(TQCodec), I, I, I, ctypes.POINTER(ctypes.c_uint32), P]
+    L.tq_encode_kv_workspace.restype = SZ
+    L.tq_encode_kv_workspace.argtypes = [ctypes.POINTER(TQCodec), ctypes.POINTER(TQCodec), I64]
     L.tq_encode_kv.restype = I
     L.tq_encode_kv.argtypes = [ctypes.POINTER(TQCodec), ctypes.POINTER(TQCodec), P, P, I, I64,
                                ctypes.POINTER(TQRope), ctypes.POINTER(TQPacked),
-                               ctypes.POINTER(TQPacked), P]
+                               ctypes.POINTER(TQPacked), P, SZ, P]
     L.tq_attend_decode_workspace.restype = SZ
     L.tq_attend_decode_workspace.argtypes = [I, I, I, I, I64, I]
     L.tq_attend_decode.restype = I
@@ -189,10 +192,18 @@ class Packed:
                                _ptr(self.rnorm).value)
 
 
-def encode_kv(kcodec, vcodec, k, v, rope=None, kout=None, vout=None, stream=None):
+def encode_workspace_bytes(kcodec, vcodec, n):
+    return int(lib().tq_encode_kv_workspace(ctypes.byref(kcodec.struct) if kcodec else None,
+                                            ctypes.byref(vcodec.struct) if vcodec else None,
+                                            int(n)))
+
+
+def encode_kv(kcodec, vcodec, k, v, rope=None, kout=None, vout=None, workspace=None,
+              stream=None):
     """Encode rows of k with kcodec and rows of v with vcodec (either side may
     be None).  k / v: device tensors [..., d], fp16 or fp32.  rope: None or
-    (base, seq_len), applied to k.  Returns (kout, vout) Packed."""
+    (base, seq_len), applied to k.  workspace: None (allocated here when the
+    codecs need one) or a device uint8 tensor.  Returns (kout, vout) Packed."""
     n = None
     dt = None
     for c, x in ((kcodec, k), (vcodec, v)):
@@ -217,12 +228,17 @@ def encode_kv(kcodec, vcodec, k, v, rope=None, kout=None, vout=None, stream=None
     r = None
     if rope is not None:
         r = TQRope(float(rope[0]), 0, int(rope[1]))
+    need = encode_workspace_bytes(kcodec, vcodec, n)
+    if workspace is None and need > 0:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = lib().tq_encode_kv(ctypes.byref(kcodec.struct) if kcodec else None,
                             ctypes.byref(vcodec.struct) if vcodec else None,
                             _ptr(k) if kcodec else None, _ptr(v) if vcodec else None, dt, n,
                             ctypes.byref(r) if r is not None else None,
                             ctypes.byref(kout.struct) if kcodec else None,
-                            ctypes.byref(vout.struct) if vcodec else None, _stream(stream))
+                            ctypes.byref(vout.struct) if vcodec else None, _ptr(workspace),
+                            wbytes, _stream(stream))
     _check(st, "tq_encode_kv")
     return kout, vout
 

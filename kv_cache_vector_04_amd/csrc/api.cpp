@@ -11,7 +11,7 @@ namespace {
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
-bool gpu_dim(int d) { return d == 64 || d == 128; }
+bool gpu_dim(int d) { return d == 64 || d == 128 || d == 1536; }
 
 int check_codec(const tq_codec* c) {
   if (c == nullptr) return TQ_ERR_INVALID_ARG;
@@ -32,7 +32,7 @@ int check_planes(const tq_codec* c, const tq_packed* p) {
     return TQ_ERR_INVALID_ARG;
   if (c->mode == TQ_PROD) {
     if (p->qjl == nullptr || p->rnorm == nullptr) return TQ_ERR_INVALID_ARG;
-    if (!aligned(p->qjl, 8) || !aligned(p->rnorm, 4)) return TQ_ERR_INVALID_ARG;
+    if (!aligned(p->qjl, c->d == 1536 ? 16 : 8) || !aligned(p->rnorm, 4)) return TQ_ERR_INVALID_ARG;
   }
   return TQ_OK;
 }
@@ -62,10 +62,29 @@ int device_cu_count() {
 }
 }  // namespace tqk
 
+namespace {
+
+size_t encode_need(const tq_codec* kc, const tq_codec* vc, int64_t n_rows) {
+  size_t need = 0;
+  for (const tq_codec* c : {kc, vc}) {
+    if (c == nullptr) continue;
+    const size_t b = tqk::wide_encode_workspace_bytes(*c, n_rows);
+    if (b > need) need = b;
+  }
+  return need;
+}
+
+}  // namespace
+
+extern "C" size_t tq_encode_kv_workspace(const tq_codec* kc, const tq_codec* vc, int64_t n_rows) {
+  if (n_rows <= 0) return 0;
+  return encode_need(kc, vc, n_rows);
+}
+
 extern "C" int tq_encode_kv(const tq_codec* kc, const tq_codec* vc, const void* k,
                             const void* v, int dtype, int64_t n_rows, const tq_rope* rope,
-                            const tq_packed* kout, const tq_packed* vout,
-                            tq_stream_t stream) {
+                            const tq_packed* kout, const tq_packed* vout, void* workspace,
+                            size_t workspace_bytes, tq_stream_t stream) {
   if (kc == nullptr && vc == nullptr) return TQ_ERR_INVALID_ARG;
   if (n_rows < 0) return TQ_ERR_INVALID_ARG;
   if (dtype != TQ_F16 && dtype != TQ_F32) return TQ_ERR_INVALID_ARG;
@@ -85,11 +104,14 @@ extern "C" int tq_encode_kv(const tq_codec* kc, const tq_codec* vc, const void* 
     if (xs[s] == nullptr || !aligned(xs[s], 16)) return TQ_ERR_INVALID_ARG;
   }
   if (n_rows == 0) return TQ_OK;
+  const size_t need = encode_need(kc, vc, n_rows);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256)))
+    return TQ_ERR_WORKSPACE;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   for (int s = 0; s < 2; ++s) {
     if (cs[s] == nullptr) continue;
     const tqk::RopeHost rh = s == 0 ? rope_of(rope) : tqk::RopeHost{};
-    const int st = hip_status(tqk::launch_encode(*cs[s], xs[s], dtype, n_rows, rh, *outs[s], hs));
+    const int st = hip_status(tqk::launch_encode(*cs[s], xs[s], dtype, n_rows, rh, *outs[s], workspace, hs));
     if (st != TQ_OK) return st;
   }
   return TQ_OK;
@@ -112,6 +134,7 @@ extern "C" int tq_attend_decode(const tq_codec* kc, const tq_codec* vc, const vo
   if ((st = check_codec(vc)) != TQ_OK) return st;
   if (kc->mode != TQ_PROD || vc->mode != TQ_MSE) return TQ_ERR_UNSUPPORTED;
   if (kc->d != vc->d) return TQ_ERR_INVALID_ARG;
+  if (kc->d != 64 && kc->d != 128) return TQ_ERR_UNSUPPORTED;   // attention kernels: d = 64, 128
   if (q == nullptr || out == nullptr || !aligned(q, 16) || !aligned(out, 16))
     return TQ_ERR_INVALID_ARG;
   if (q_dtype != TQ_F16 && q_dtype != TQ_F32) return TQ_ERR_INVALID_ARG;
@@ -149,6 +172,9 @@ extern "C" int tq_inner_product(const tq_codec* c, const void* q, int q_dtype, i
   if (top_k == 0 && out == nullptr) return TQ_ERR_INVALID_ARG;
   if (top_k > n) return TQ_ERR_INVALID_ARG;
   if ((st = check_planes(c, x)) != TQ_OK) return st;
+  // d = 1536 with 1-bit codes scores with +-1 operands: the table must be symmetric
+  if (c->d == 1536 && c->code_bits == 1 && !(c->centroids[0] == -c->centroids[1] && c->centroids[1] > 0.f))
+    return TQ_ERR_UNSUPPORTED;
   const size_t need = tqk::scan_workspace_bytes(n_q, n, c->d, top_k);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16)))
     return TQ_ERR_WORKSPACE;

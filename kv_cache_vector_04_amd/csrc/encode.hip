@@ -809,8 +809,10 @@ static bool build_grid(const tq_codec& c, EncodeParams& p) {
 }
 
 hipError_t launch_encode(const tq_codec& c, const void* x, int dtype, int64_t n_rows,
-                         const RopeHost& rope, const tq_packed& out, hipStream_t stream) {
+                         const RopeHost& rope, const tq_packed& out, void* workspace,
+                         hipStream_t stream) {
   if (n_rows == 0) return hipSuccess;
+  if (c.d == 1536) return launch_wide_encode(c, x, dtype, n_rows, out, workspace, stream);
   EncodeParams p = {};
   p.x = x;
   p.n_rows = n_rows;

@@ -19,7 +19,18 @@ struct RopeHost {
 // Encode n_rows rows of one tensor with one codec.
 hipError_t launch_encode(const tq_codec& c, const void* x, int dtype,
                          int64_t n_rows, const RopeHost& rope,
-                         const tq_packed& out, hipStream_t stream);
+                         const tq_packed& out, void* workspace, hipStream_t stream);
+
+// d = 1536 (wide.hip).  The encode workspace holds S as fp16 hi / lo planes
+// and the residual planes of one block of vectors (prod only); the scan
+// workspace holds the S planes and the four query planes.
+size_t wide_encode_workspace_bytes(const tq_codec& c, int64_t n_rows);
+hipError_t launch_wide_encode(const tq_codec& c, const void* x, int dtype, int64_t n_rows,
+                              const tq_packed& out, void* workspace, hipStream_t stream);
+size_t wide_scan_workspace_bytes(int64_t n_q);
+hipError_t launch_wide_scan(const tq_codec& c, const void* q, int q_dtype, int64_t n_q,
+                            const tq_packed& x, int64_t n, float* scores, void* workspace,
+                            hipStream_t stream);
 
 size_t attend_workspace_bytes(int batch, int n_q, int hq, int hkv, int64_t ctx, int d);
 hipError_t launch_attend(const tq_codec& kc, const tq_codec& vc, const void* q,

@@ -85,23 +85,56 @@ def test_encode_validation_before_launch(L):
     pk = tq.TQPacked(1 << 20, 1 << 20, 1 << 20, 1 << 20)
     pv = tq.TQPacked(1 << 20, None, 1 << 20, None)
     enc = L.tq_encode_kv
-    assert enc(None, None, fake, fake, 0, 10, None, None, None, None) == tq.TQ_ERR_INVALID_ARG
-    assert enc(ctypes.byref(kc), None, fake, None, 0, -1, None, ctypes.byref(pk), None, None) == tq.TQ_ERR_INVALID_ARG
-    assert enc(ctypes.byref(kc), None, fake, None, 7, 10, None, ctypes.byref(pk), None, None) == tq.TQ_ERR_INVALID_ARG
+    assert enc(None, None, fake, fake, 0, 10, None, None, None, None, 0, None) == tq.TQ_ERR_INVALID_ARG
+    assert enc(ctypes.byref(kc), None, fake, None, 0, -1, None, ctypes.byref(pk), None, None, 0, None) == tq.TQ_ERR_INVALID_ARG
+    assert enc(ctypes.byref(kc), None, fake, None, 7, 10, None, ctypes.byref(pk), None, None, 0, None) == tq.TQ_ERR_INVALID_ARG
     # misaligned input, missing planes
     assert enc(ctypes.byref(kc), None, ctypes.c_void_p((1 << 20) + 2), None, 0, 10, None,
-               ctypes.byref(pk), None, None) == tq.TQ_ERR_INVALID_ARG
-    assert enc(ctypes.byref(kc), None, fake, None, 0, 10, None, ctypes.byref(pv), None, None) == tq.TQ_ERR_INVALID_ARG
+               ctypes.byref(pk), None, None, 0, None) == tq.TQ_ERR_INVALID_ARG
+    assert enc(ctypes.byref(kc), None, fake, None, 0, 10, None, ctypes.byref(pv), None, None, 0, None) == tq.TQ_ERR_INVALID_ARG
     # RoPE only on the d = 64 fp16 key path
     rope = tq.TQRope(10000.0, 0, 1024)
     assert enc(ctypes.byref(kc), None, fake, None, 0, 10, ctypes.byref(rope), ctypes.byref(pk),
-               None, None) == tq.TQ_ERR_UNSUPPORTED
+               None, None, 0, None) == tq.TQ_ERR_UNSUPPORTED
     # n_rows = 0 is a valid no-op that launches nothing
     assert enc(ctypes.byref(kc), ctypes.byref(vc), fake, fake, 0, 0, None, ctypes.byref(pk),
-               ctypes.byref(pv), None) == tq.TQ_OK
+               ctypes.byref(pv), None, 0, None) == tq.TQ_OK
     # a dimension with no GPU kernel
     bad = _codec_struct(L, 96, tq.TQ_MSE, 2)
-    assert enc(None, ctypes.byref(bad), None, fake, 0, 10, None, None, ctypes.byref(pv), None) == tq.TQ_ERR_UNSUPPORTED
+    assert enc(None, ctypes.byref(bad), None, fake, 0, 10, None, None, ctypes.byref(pv), None, 0, None) == tq.TQ_ERR_UNSUPPORTED
+    # d = 128 and mse codecs need no workspace
+    assert L.tq_encode_kv_workspace(ctypes.byref(kc), ctypes.byref(vc), 1 << 20) == 0
+    assert L.tq_encode_kv_workspace(None, ctypes.byref(_codec_struct(L, 1536, tq.TQ_MSE, 2)), 1 << 20) == 0
+
+
+def test_wide_encode_workspace(L):
+    kw = _codec_struct(L, 1536, tq.TQ_PROD, 2)
+    fake = ctypes.c_void_p(1 << 20)
+    pk = tq.TQPacked(1 << 20, 1 << 20, 1 << 20, 1 << 20)
+    # S planes (2 x 1536^2 fp16) + residual planes (2 x 1536 fp16 per vector) of one block
+    s_planes = 2 * 1536 * 1536 * 2
+    assert L.tq_encode_kv_workspace(ctypes.byref(kw), None, 10) == s_planes + (10 * 1536 * 4 + 255) // 256 * 256
+    big = L.tq_encode_kv_workspace(ctypes.byref(kw), None, 1 << 24)
+    assert big == L.tq_encode_kv_workspace(ctypes.byref(kw), None, 1 << 22)     # blocks bound it
+    assert L.tq_encode_kv_workspace(ctypes.byref(kw), None, 0) == 0
+    need = L.tq_encode_kv_workspace(ctypes.byref(kw), None, 10)
+    enc = L.tq_encode_kv
+    assert enc(ctypes.byref(kw), None, fake, None, 1, 10, None, ctypes.byref(pk), None, None, 0,
+               None) == tq.TQ_ERR_WORKSPACE
+    assert enc(ctypes.byref(kw), None, fake, None, 1, 10, None, ctypes.byref(pk), None, fake, need - 1,
+               None) == tq.TQ_ERR_WORKSPACE
+    assert enc(ctypes.byref(kw), None, fake, None, 1, 10, None, ctypes.byref(pk), None,
+               ctypes.c_void_p((1 << 20) + 16), need, None) == tq.TQ_ERR_WORKSPACE     # not 256-aligned
+    # qjl rows of 192 bytes must be 16-byte aligned at d = 1536
+    pk8 = tq.TQPacked(1 << 20, (1 << 20) + 8, 1 << 20, 1 << 20)
+    assert enc(ctypes.byref(kw), None, fake, None, 1, 10, None, ctypes.byref(pk8), None, fake, need,
+               None) == tq.TQ_ERR_INVALID_ARG
+    # attention has no d = 1536 kernel
+    vw = _codec_struct(L, 1536, tq.TQ_MSE, 2)
+    pv = tq.TQPacked(1 << 20, None, 1 << 20, None)
+    assert L.tq_attend_decode(ctypes.byref(kw), ctypes.byref(vw), fake, 0, 1, 1, 1, 1, None,
+                              ctypes.byref(pk), ctypes.byref(pv), 16, 0.0, fake, None, fake, 1 << 30,
+                              None) == tq.TQ_ERR_UNSUPPORTED
 
 
 def test_attend_and_scan_validation(L):
