@@ -277,16 +277,25 @@ def inner_product_workspace_bytes(n_q, n, d, top_k):
     return int(lib().tq_inner_product_workspace(n_q, n, d, top_k))
 
 
-def inner_product(codec, q, pk, n, top_k=0, want_matrix=True, workspace=None, stream=None):
+def inner_product(codec, q, pk, n, top_k=0, want_matrix=True, workspace=None, stream=None,
+                  out_ids=None, out_vals=None):
     """Estimated inner products of q [n_q, d] against n packed rows.  Returns
-    the [n_q, n] matrix (if want_matrix) and, for top_k > 0, (ids, scores)."""
+    the [n_q, n] matrix (if want_matrix) and, for top_k > 0, (ids, scores)
+    (written into out_ids / out_vals when given)."""
     _device_tensor(q, "q")
     n_q, d = q.shape
     out = torch.empty((n_q, n), dtype=torch.float32, device=q.device) if want_matrix else None
     ids = vals = None
     if top_k:
-        ids = torch.empty((n_q, top_k), dtype=torch.int64, device=q.device)
-        vals = torch.empty((n_q, top_k), dtype=torch.float32, device=q.device)
+        ids = out_ids if out_ids is not None else \
+            torch.empty((n_q, top_k), dtype=torch.int64, device=q.device)
+        vals = out_vals if out_vals is not None else \
+            torch.empty((n_q, top_k), dtype=torch.float32, device=q.device)
+        _device_tensor(ids, "out_ids")
+        _device_tensor(vals, "out_vals")
+        if ids.shape != (n_q, top_k) or vals.shape != (n_q, top_k) or ids.dtype != torch.int64 \
+                or vals.dtype != torch.float32:
+            raise ValueError("out_ids / out_vals must be [n_q, top_k] int64 / float32")
     need = inner_product_workspace_bytes(n_q, n, d, top_k)
     if workspace is None:
         workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)

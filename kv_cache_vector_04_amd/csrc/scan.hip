@@ -102,13 +102,13 @@ __global__ __launch_bounds__(kScanRows) void scan_kernel(ScanParams p) {
 }
 
 // ---- top-k ---------------------------------------------------------------
-// Two passes.  Pass 1: one wavefront per (query, chunk of rows) keeps, per
-// lane, a sorted list of its best k (descending score, ties to the lower row
-// index), then merges the 64 lists with k wave-wide arg-max rounds into the
-// chunk's k candidates.  Pass 2 runs the same wavefront routine over the
+// Two passes.  Pass 1: one wavefront per (query, chunk of rows) keeps the
+// chunk's best k as a sorted list spread over lanes 0..k-1 (descending
+// score, ties to the lower row index).  Items stream through in batches; a
+// ballot against the list's k-th entry picks the few that can enter, and each
+// enters with one wave-wide shift.  Pass 2 runs the same routine over the
 // candidates of all chunks of a query.  Lists shorter than k are padded with
 // (-inf, INT64_MAX), which every real entry beats.
-constexpr int kTopMax = 64;
 
 struct TopKParams {
   const float* val;      // pass 1: scores [n_q][len]; pass 2: candidates [n_q][len]
@@ -125,10 +125,48 @@ __device__ __forceinline__ bool better(float v1, int64_t i1, float v2, int64_t i
   return v1 > v2 || (v1 == v2 && i1 < i2);
 }
 
-template <int KM>
+__device__ __forceinline__ int64_t readlane64(int64_t x, int l) {
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)(uint64_t)x, l);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)((uint64_t)x >> 32), l);
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+struct WaveTopK {
+  float lv = -INFINITY;          // lane i < k: the i-th best so far
+  int64_t li = INT64_MAX;
+  float tv = -INFINITY;          // the k-th best (wave-uniform)
+  int64_t ti = INT64_MAX;
+
+  // offer one item per lane; the lanes whose item beats the k-th best enter
+  // one at a time
+  __device__ __forceinline__ void offer(float v, int64_t id, int k, int lane) {
+    uint64_t m = __ballot(better(v, id, tv, ti));
+    while (m) {
+      const int src = __builtin_ctzll(m);
+      m &= m - 1;
+      const float x = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
+      const int64_t xi = readlane64(id, src);
+      if (!better(x, xi, tv, ti)) continue;            // the bound rose meanwhile
+      // entries that beat x form a prefix of the sorted list
+      const uint64_t ahead = __ballot(lane < k && better(lv, li, x, xi));
+      const int pos = __popcll(ahead);
+      const float uv = __shfl_up(lv, 1);
+      const int64_t ui = __shfl_up(li, 1);
+      if (lane > pos) {
+        lv = uv;
+        li = ui;
+      } else if (lane == pos) {
+        lv = x;
+        li = xi;
+      }
+      tv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lv), k - 1));
+      ti = readlane64(li, k - 1);
+    }
+  }
+};
+
+template <bool VEC>
 __global__ __launch_bounds__(kWave) void topk_kernel(TopKParams p) {
-  __shared__ float s_val[kWave][KM];
-  __shared__ int64_t s_id[kWave][KM];
   const int lane = threadIdx.x;
   const int64_t qa = blockIdx.x / p.nchunks;
   const int c = (int)(blockIdx.x % p.nchunks);
@@ -137,60 +175,47 @@ __global__ __launch_bounds__(kWave) void topk_kernel(TopKParams p) {
   const float* val = p.val + qa * p.len;
   const int64_t* ids = p.id != nullptr ? p.id + qa * p.len : nullptr;
   const int k = p.k;
-  int cnt = 0;
-  float kv = -INFINITY;          // the lane's k-th entry once its list is full
-  int64_t ki = INT64_MAX;
-  for (int64_t j0 = beg + lane; j0 < end; j0 += 4 * kWave) {
-    float v[4];
-    int64_t id[4];
+  WaveTopK t;
+  constexpr int U = 16;
+  if constexpr (VEC) {
+    // 16-byte aligned rows and chunks: 16 float4 loads (64 items) in flight per lane
+    for (int64_t j0 = beg + 4 * lane; j0 < end; j0 += 4 * U * kWave) {
+      float4 v[U];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t j = j0 + u * kWave;
-      const bool in = j < end;
-      v[u] = in ? val[j] : -INFINITY;
-      id[u] = in ? (ids != nullptr ? ids[j] : j) : INT64_MAX;
+      for (int u = 0; u < U; ++u) {
+        const int64_t j = j0 + 4 * u * kWave;
+        v[u] = j < end ? *reinterpret_cast<const float4*>(val + j)
+                       : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t j = j0 + 4 * u * kWave;
+        const bool in = j < end;
+        t.offer(v[u].x, in ? j : INT64_MAX, k, lane);
+        t.offer(v[u].y, in ? j + 1 : INT64_MAX, k, lane);
+        t.offer(v[u].z, in ? j + 2 : INT64_MAX, k, lane);
+        t.offer(v[u].w, in ? j + 3 : INT64_MAX, k, lane);
+      }
     }
+  } else {
+    for (int64_t j0 = beg + lane; j0 < end; j0 += U * kWave) {
+      float v[U];
+      int64_t id[U];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (id[u] == INT64_MAX) continue;                    // padding
-      if (cnt == k && !better(v[u], id[u], kv, ki)) continue;
-      int pos = cnt < k ? cnt : k - 1;
-      while (pos > 0 && better(v[u], id[u], s_val[lane][pos - 1], s_id[lane][pos - 1])) {
-        s_val[lane][pos] = s_val[lane][pos - 1];
-        s_id[lane][pos] = s_id[lane][pos - 1];
-        --pos;
+      for (int u = 0; u < U; ++u) {
+        const int64_t j = j0 + u * kWave;
+        const bool in = j < end;
+        v[u] = in ? val[j] : -INFINITY;
+        id[u] = in ? (ids != nullptr ? ids[j] : j) : INT64_MAX;
       }
-      s_val[lane][pos] = v[u];
-      s_id[lane][pos] = id[u];
-      if (cnt < k) ++cnt;
-      if (cnt == k) {
-        kv = s_val[lane][k - 1];
-        ki = s_id[lane][k - 1];
-      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) t.offer(v[u], id[u], k, lane);
     }
   }
-  int head = 0;
-  float* ov = p.oval + ((int64_t)qa * p.nchunks + c) * k;
-  int64_t* oi = p.oid + ((int64_t)qa * p.nchunks + c) * k;
-  for (int r = 0; r < k; ++r) {
-    float bv = head < cnt ? s_val[lane][head] : -INFINITY;
-    int64_t bi = head < cnt ? s_id[lane][head] : INT64_MAX;
-    int bl = lane;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float xv = __shfl_xor(bv, off);
-      const int64_t xi = __shfl_xor(bi, off);
-      const int xl = __shfl_xor(bl, off);
-      const bool take = better(xv, xi, bv, bi) || (xv == bv && xi == bi && xl < bl);
-      bv = take ? xv : bv;
-      bi = take ? xi : bi;
-      bl = take ? xl : bl;
-    }
-    if (lane == bl) ++head;
-    if (lane == 0) {
-      ov[r] = bv;
-      oi[r] = bi;
-    }
+  if (lane < k) {
+    const int64_t o = ((int64_t)qa * p.nchunks + c) * k + lane;
+    p.oval[o] = t.lv;
+    p.oid[o] = t.li;
   }
 }
 
@@ -243,10 +268,11 @@ static hipError_t pick_scan(int cb, bool prod, const ScanParams& p, hipStream_t 
 
 static hipError_t run_topk(const TopKParams& t, int64_t n_q, hipStream_t s) {
   const unsigned blocks = (unsigned)(n_q * t.nchunks);
-  if (t.k <= 16)
-    hipLaunchKernelGGL(topk_kernel<16>, dim3(blocks), dim3(kWave), 0, s, t);
-  else
-    hipLaunchKernelGGL(topk_kernel<kTopMax>, dim3(blocks), dim3(kWave), 0, s, t);
+  // float4 loads need 16-byte aligned query rows and chunk starts
+  const bool vec = t.id == nullptr && t.len % 4 == 0 && t.chunk % 4 == 0 &&
+                   ((uintptr_t)t.val % 16) == 0;
+  if (vec) hipLaunchKernelGGL((topk_kernel<true>), dim3(blocks), dim3(kWave), 0, s, t);
+  else hipLaunchKernelGGL((topk_kernel<false>), dim3(blocks), dim3(kWave), 0, s, t);
   return hipGetLastError();
 }
 
@@ -292,7 +318,8 @@ hipError_t launch_scan(const tq_codec& c, const void* q, int q_dtype, int64_t n_
   const size_t cand = (size_t)n_q * nch * top_k;
   float* cval = reinterpret_cast<float*>(ws + off);
   int64_t* cid = reinterpret_cast<int64_t*>(ws + off + align256(cand * sizeof(float)));
-  TopKParams t1 = {scores, nullptr, n, (n + nch - 1) / nch, nch, top_k, cval, cid};
+  const int64_t chunk = ((n + nch - 1) / nch + 3) / 4 * 4;
+  TopKParams t1 = {scores, nullptr, n, chunk, nch, top_k, cval, cid};
   if ((e = run_topk(t1, n_q, stream)) != hipSuccess) return e;
   const int64_t len2 = (int64_t)nch * top_k;
   TopKParams t2 = {cval, cid, len2, len2, 1, top_k, top_scores, top_ids};

@@ -537,64 +537,75 @@ __global__ __launch_bounds__(64 * kSWaves) void wide_scan_kernel(WScanParams p) 
       accq[rb][v] = 0.f;
     }
 
-  for (int c = 0; c < kWA; ++c) {
-    // this chunk's code bits (8 CB bytes per row) and sign bits (8 bytes)
-    uint32_t cw[kSRB][2 * CB];
-    uint2 sw[kSRB];
+  // Half chunks of 64 coordinates (four k steps): the operands of half
+  // chunk hc + 1 load while the products of hc run.  Lane half h covers
+  // coordinates 128 c + 64 h + 32 (hc % 2) + [0, 32): 64 contiguous bytes of
+  // each query plane and 4 CB contiguous bytes of each code row.
+  half8_t fa[2][4][4];              // [buffer][k step][qh, ql, sh, sl]
+  uint32_t cw[2][kSRB][CB];         // code bits of the half chunk
+  uint32_t sw[2][kSRB];             // sign bits
+  auto load = [&](int hc, int bf) {
+    const int c = hc >> 1, hh = hc & 1;
+    const int ko = 128 * c + 32 * hh;
 #pragma unroll
-    for (int rb = 0; rb < kSRB; ++rb) {
-      const uint2* src = reinterpret_cast<const uint2*>(crow[rb] + 16 * CB * c + 8 * CB * h);
-#pragma unroll
-      for (int u = 0; u < CB; ++u) {
-        const uint2 v = src[u];
-        cw[rb][2 * u] = v.x;
-        cw[rb][2 * u + 1] = v.y;
+    for (int s = 0; s < 4; ++s) {
+      fa[bf][s][0] = *reinterpret_cast<const half8_t*>(aqh + ko + 8 * s);
+      fa[bf][s][1] = *reinterpret_cast<const half8_t*>(aql + ko + 8 * s);
+      if constexpr (PROD) {
+        fa[bf][s][2] = *reinterpret_cast<const half8_t*>(ash + ko + 8 * s);
+        fa[bf][s][3] = *reinterpret_cast<const half8_t*>(asl + ko + 8 * s);
       }
-      if constexpr (PROD) sw[rb] = *reinterpret_cast<const uint2*>(srow[rb] + 16 * c + 8 * h);
     }
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int ko = 128 * c + 8 * s;
-      const half8_t fqh = *reinterpret_cast<const half8_t*>(aqh + ko);
-      const half8_t fql = *reinterpret_cast<const half8_t*>(aql + ko);
-      half8_t fsh, fsl;
-      if constexpr (PROD) {
-        fsh = *reinterpret_cast<const half8_t*>(ash + ko);
-        fsl = *reinterpret_cast<const half8_t*>(asl + ko);
-      }
+    for (int rb = 0; rb < kSRB; ++rb) {
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(crow[rb] + 16 * CB * c + 8 * CB * h + 4 * CB * hh);
+#pragma unroll
+      for (int u = 0; u < CB; ++u) cw[bf][rb][u] = src[u];
+      if constexpr (PROD) sw[bf][rb] = *reinterpret_cast<const uint32_t*>(srow[rb] + 16 * c + 8 * h + 4 * hh);
+    }
+  };
+  auto compute = [&](int bf) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
 #pragma unroll
       for (int rb = 0; rb < kSRB; ++rb) {
         if constexpr (CB == 1) {
-          const uint32_t byte = (cw[rb][s >> 2] >> (8 * (s & 3))) & 0xffu;
-          const half8_t cb = pm1_frag(byte);
-          accm[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fqh, cb, accm[rb], 0, 0, 0);
-          accm[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fql, cb, accm[rb], 0, 0, 0);
+          const half8_t cb = pm1_frag((cw[bf][rb][0] >> (8 * s)) & 0xffu);
+          accm[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[bf][s][0], cb, accm[rb], 0, 0, 0);
+          accm[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[bf][s][1], cb, accm[rb], 0, 0, 0);
         } else {
           uint32_t hi[4], lo[4];
 #pragma unroll
           for (int pp = 0; pp < 4; ++pp) {
-            const int off = (8 * s + 2 * pp) * CB;     // bit offset in this lane's piece
+            const int off = (8 * s + 2 * pp) * CB;     // bit offset in this lane's half-chunk bits
             const int w = off >> 5, sh = off & 31;
-            uint32_t e = cw[rb][w] >> sh;
-            if (sh + 2 * CB > 32) e |= cw[rb][w + 1] << (32 - sh);
+            uint32_t e = cw[bf][rb][w] >> sh;
+            if (sh + 2 * CB > 32) e |= cw[bf][rb][w + 1] << (32 - sh);
             e &= NP - 1;
             hi[pp] = s_ph[e];
             lo[pp] = s_pl[e];
           }
-          const half8_t ch = __builtin_bit_cast(half8_t, make_uint4(hi[0], hi[1], hi[2], hi[3]));
-          const half8_t cl = __builtin_bit_cast(half8_t, make_uint4(lo[0], lo[1], lo[2], lo[3]));
-          accm[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fqh, ch, accm[rb], 0, 0, 0);
-          accm[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fql, ch, accm[rb], 0, 0, 0);
-          accm[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fqh, cl, accm[rb], 0, 0, 0);
+          const half8_t ch = __builtin_bit_cast(half8_t, u32x4{hi[0], hi[1], hi[2], hi[3]});
+          const half8_t cl = __builtin_bit_cast(half8_t, u32x4{lo[0], lo[1], lo[2], lo[3]});
+          accm[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[bf][s][0], ch, accm[rb], 0, 0, 0);
+          accm[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[bf][s][1], ch, accm[rb], 0, 0, 0);
+          accm[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[bf][s][0], cl, accm[rb], 0, 0, 0);
         }
         if constexpr (PROD) {
-          const uint32_t sb = ((s < 4 ? sw[rb].x : sw[rb].y) >> (8 * (s & 3))) & 0xffu;
-          const half8_t sg = pm1_frag(sb);
-          accq[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fsh, sg, accq[rb], 0, 0, 0);
-          accq[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fsl, sg, accq[rb], 0, 0, 0);
+          const half8_t sg = pm1_frag((sw[bf][rb] >> (8 * s)) & 0xffu);
+          accq[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[bf][s][2], sg, accq[rb], 0, 0, 0);
+          accq[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[bf][s][3], sg, accq[rb], 0, 0, 0);
         }
       }
     }
+  };
+  constexpr int NH = 2 * kWA;
+  load(0, 0);
+  for (int hc = 0; hc < NH; hc += 2) {
+    load(hc + 1, 1);
+    compute(0);
+    if (hc + 2 < NH) load(hc + 2, 0);
+    compute(1);
   }
 
   // est = nu (cscale M + sqrt(pi/2)/m gamma Q); element v: query 8 (v/4) + 4 h + v % 4
