@@ -484,10 +484,11 @@ __device__ __forceinline__ half8_t pm1_frag(uint32_t byte) {
 }
 
 template <int CB, bool PROD>
-__global__ __launch_bounds__(64 * kSWaves) void wide_scan_kernel(WScanParams p) {
+__global__ __launch_bounds__(64 * kSWaves, 2) void wide_scan_kernel(WScanParams p) {
   constexpr int NP = CB > 1 ? (1 << (2 * CB)) : 1;
   __shared__ uint32_t s_ph[NP];
   __shared__ uint32_t s_pl[NP];
+  __shared__ u32x4 s_pm[256];       // eight bits -> eight fp16 +-1
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
   if constexpr (CB > 1) {
     const uint32_t* chl = reinterpret_cast<const uint32_t*>(TQ_KARG(WScanParams, chl));
@@ -496,8 +497,9 @@ __global__ __launch_bounds__(64 * kSWaves) void wide_scan_kernel(WScanParams p) 
       s_ph[e] = (a & 0xffffu) | (b << 16);
       s_pl[e] = (a >> 16) | (b & 0xffff0000u);
     }
-    __syncthreads();
   }
+  for (int e = tid; e < 256; e += 64 * kSWaves) s_pm[e] = __builtin_bit_cast(u32x4, pm1_frag((uint32_t)e));
+  __syncthreads();
   const int64_t QB = (p.n_q + 31) / 32;
   const int64_t b = blockIdx.x;
   int64_t qb, rt;
@@ -537,25 +539,41 @@ __global__ __launch_bounds__(64 * kSWaves) void wide_scan_kernel(WScanParams p) 
       accq[rb][v] = 0.f;
     }
 
-  // Half chunks of 64 coordinates (four k steps): the operands of half
-  // chunk hc + 1 load while the products of hc run.  Lane half h covers
-  // coordinates 128 c + 64 h + 32 (hc % 2) + [0, 32): 64 contiguous bytes of
-  // each query plane and 4 CB contiguous bytes of each code row.
-  half8_t fa[2][4][4];              // [buffer][k step][qh, ql, sh, sl]
-  uint32_t cw[2][kSRB][CB];         // code bits of the half chunk
-  uint32_t sw[2][kSRB];             // sign bits
-  auto load = [&](int hc, int bf) {
+  // k steps of 16 coordinates, four to a half chunk of 64: in half chunk hc
+  // (chunk c = hc / 2) lane half h covers coordinates
+  // 128 c + 64 h + 32 (hc % 2) + [0, 32), 8 per k step.  The workgroup's 32
+  // query rows of a half chunk pass through LDS (double buffered, one
+  // barrier per half chunk); the next half chunk's query planes and code bits
+  // load while the current products run.
+  constexpr int NPL = PROD ? 4 : 2;            // query planes
+  constexpr int QS = 72;                       // halves per LDS row (64 + 8 pad)
+  __shared__ __align__(16) _Float16 s_q[2][NPL][32][QS];
+  const _Float16* planes[4] = {p.qh, p.ql, p.sh, p.sl};
+  constexpr int QPIECES = NPL * 32 * 8 / (64 * kSWaves);   // 16-byte pieces per thread
+  u32x4 qr[QPIECES];
+  auto gload_q = [&](int hc) {
     const int c = hc >> 1, hh = hc & 1;
-    const int ko = 128 * c + 32 * hh;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      fa[bf][s][0] = *reinterpret_cast<const half8_t*>(aqh + ko + 8 * s);
-      fa[bf][s][1] = *reinterpret_cast<const half8_t*>(aql + ko + 8 * s);
-      if constexpr (PROD) {
-        fa[bf][s][2] = *reinterpret_cast<const half8_t*>(ash + ko + 8 * s);
-        fa[bf][s][3] = *reinterpret_cast<const half8_t*>(asl + ko + 8 * s);
-      }
+    for (int u = 0; u < QPIECES; ++u) {
+      const int t = tid + u * 64 * kSWaves;
+      const int pl = t >> 8, row = (t >> 3) & 31, j = t & 7;
+      const int64_t qa2 = qb * 32 + row;
+      const _Float16* src = planes[pl] + (qa2 < p.n_q ? qa2 : 0) * kWD + 128 * c + 64 * (j >> 2) + 32 * hh + 8 * (j & 3);
+      qr[u] = *reinterpret_cast<const u32x4*>(src);
     }
+  };
+  auto lstore_q = [&](int bf) {
+#pragma unroll
+    for (int u = 0; u < QPIECES; ++u) {
+      const int t = tid + u * 64 * kSWaves;
+      const int pl = t >> 8, row = (t >> 3) & 31, j = t & 7;
+      *reinterpret_cast<u32x4*>(&s_q[bf][pl][row][32 * (j >> 2) + 8 * (j & 3)]) = qr[u];
+    }
+  };
+  uint32_t cw[2][kSRB][CB];         // code bits of a half chunk
+  uint32_t sw[2][kSRB];             // sign bits
+  auto load_bits = [&](int hc, int bf) {
+    const int c = hc >> 1, hh = hc & 1;
 #pragma unroll
     for (int rb = 0; rb < kSRB; ++rb) {
       const uint32_t* src = reinterpret_cast<const uint32_t*>(crow[rb] + 16 * CB * c + 8 * CB * h + 4 * CB * hh);
@@ -564,48 +582,60 @@ __global__ __launch_bounds__(64 * kSWaves) void wide_scan_kernel(WScanParams p) 
       if constexpr (PROD) sw[bf][rb] = *reinterpret_cast<const uint32_t*>(srow[rb] + 16 * c + 8 * h + 4 * hh);
     }
   };
-  auto compute = [&](int bf) {
+  auto compute = [&](int s, int bf) {
+    half8_t fa[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int pl = 0; pl < NPL; ++pl)
+      fa[pl] = *reinterpret_cast<const half8_t*>(&s_q[bf][pl][lane & 31][32 * h + 8 * s]);
 #pragma unroll
-      for (int rb = 0; rb < kSRB; ++rb) {
-        if constexpr (CB == 1) {
-          const half8_t cb = pm1_frag((cw[bf][rb][0] >> (8 * s)) & 0xffu);
-          accm[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[bf][s][0], cb, accm[rb], 0, 0, 0);
-          accm[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[bf][s][1], cb, accm[rb], 0, 0, 0);
-        } else {
-          uint32_t hi[4], lo[4];
+    for (int rb = 0; rb < kSRB; ++rb) {
+      if constexpr (CB == 1) {
+        const half8_t cb = __builtin_bit_cast(half8_t, s_pm[(cw[bf][rb][0] >> (8 * s)) & 0xffu]);
+        accm[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[0], cb, accm[rb], 0, 0, 0);
+        accm[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[1], cb, accm[rb], 0, 0, 0);
+      } else {
+        uint32_t hi[4], lo[4];
 #pragma unroll
-          for (int pp = 0; pp < 4; ++pp) {
-            const int off = (8 * s + 2 * pp) * CB;     // bit offset in this lane's half-chunk bits
-            const int w = off >> 5, sh = off & 31;
-            uint32_t e = cw[bf][rb][w] >> sh;
-            if (sh + 2 * CB > 32) e |= cw[bf][rb][w + 1] << (32 - sh);
-            e &= NP - 1;
-            hi[pp] = s_ph[e];
-            lo[pp] = s_pl[e];
-          }
-          const half8_t ch = __builtin_bit_cast(half8_t, u32x4{hi[0], hi[1], hi[2], hi[3]});
-          const half8_t cl = __builtin_bit_cast(half8_t, u32x4{lo[0], lo[1], lo[2], lo[3]});
-          accm[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[bf][s][0], ch, accm[rb], 0, 0, 0);
-          accm[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[bf][s][1], ch, accm[rb], 0, 0, 0);
-          accm[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[bf][s][0], cl, accm[rb], 0, 0, 0);
+        for (int pp = 0; pp < 4; ++pp) {
+          const int off = (8 * s + 2 * pp) * CB;     // bit offset in this lane's half-chunk bits
+          const int w = off >> 5, sh = off & 31;
+          uint32_t e = cw[bf][rb][w] >> sh;
+          if (sh + 2 * CB > 32) e |= cw[bf][rb][w + 1] << (32 - sh);
+          e &= NP - 1;
+          hi[pp] = s_ph[e];
+          lo[pp] = s_pl[e];
         }
-        if constexpr (PROD) {
-          const half8_t sg = pm1_frag((sw[bf][rb] >> (8 * s)) & 0xffu);
-          accq[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[bf][s][2], sg, accq[rb], 0, 0, 0);
-          accq[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[bf][s][3], sg, accq[rb], 0, 0, 0);
-        }
+        const half8_t ch = __builtin_bit_cast(half8_t, u32x4{hi[0], hi[1], hi[2], hi[3]});
+        const half8_t cl = __builtin_bit_cast(half8_t, u32x4{lo[0], lo[1], lo[2], lo[3]});
+        accm[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[0], ch, accm[rb], 0, 0, 0);
+        accm[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[1], ch, accm[rb], 0, 0, 0);
+        accm[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[0], cl, accm[rb], 0, 0, 0);
+      }
+      if constexpr (PROD) {
+        const half8_t sg = __builtin_bit_cast(half8_t, s_pm[(sw[bf][rb] >> (8 * s)) & 0xffu]);
+        accq[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[2], sg, accq[rb], 0, 0, 0);
+        accq[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[3], sg, accq[rb], 0, 0, 0);
       }
     }
   };
-  constexpr int NH = 2 * kWA;
-  load(0, 0);
+  constexpr int NH = 2 * kWA;       // half chunks
+  gload_q(0);
+  load_bits(0, 0);
+  lstore_q(0);
+  __syncthreads();
+  auto half = [&](int hc, int bf) {
+    if (hc + 1 < NH) {
+      gload_q(hc + 1);
+      load_bits(hc + 1, bf ^ 1);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) compute(s, bf);
+    if (hc + 1 < NH) lstore_q(bf ^ 1);
+    __syncthreads();
+  };
   for (int hc = 0; hc < NH; hc += 2) {
-    load(hc + 1, 1);
-    compute(0);
-    if (hc + 2 < NH) load(hc + 2, 0);
-    compute(1);
+    half(hc, 0);
+    half(hc + 1, 1);
   }
 
   // est = nu (cscale M + sqrt(pi/2)/m gamma Q); element v: query 8 (v/4) + 4 h + v % 4
