@@ -45,14 +45,26 @@ TRAFFIC = {"encode_k": (33138 * 2 + 18432) * 1024,
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 200 for gqa_decode, 3 for the others)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps (default 20 for gqa_decode, 1 for the others)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sets", type=int, default=8)
-    ap.add_argument("--workload", default="gqa_decode", choices=("gqa_decode", "vector_search"),
-                    help="gqa_decode (the default bench line) or vector_search (1e6 x d1536 "
-                         "encode + 1024-query scan with top-10)")
-    return ap.parse_args()
+    ap.add_argument("--workload", default="gqa_decode",
+                    choices=("gqa_decode", "llama_prefill", "esm2", "vector_search"),
+                    help="gqa_decode (the default bench line); llama_prefill (32 layers x 8 KV "
+                         "heads x 131072 tokens, 3-bit, encode + one decode step per layer); "
+                         "esm2 (33 layers x 64 x 20 heads x 1024 tokens, d64, RoPE keys, 3-bit, "
+                         "encode + bidirectional attention); vector_search (1e6 x d1536 encode "
+                         "+ 1024-query scan with top-10)")
+    a = ap.parse_args()
+    heavy = a.workload != "gqa_decode"
+    if a.steps is None:
+        a.steps = 3 if heavy else 200
+    if a.warmup is None:
+        a.warmup = 1 if heavy else 20
+    return a
 
 
 def main():
@@ -70,6 +82,8 @@ def main():
     torch.cuda.set_device(dev)
     if a.workload == "vector_search":
         return bench_search(a, torch, synth, tq, dev)
+    if a.workload in ("llama_prefill", "esm2"):
+        return bench_layers(a, torch, synth, tq, dev)
     hkv, ctx, d, hq = 8, 32768, 128, 32
     w = synth.gqa_decode(hkv=hkv, ctx=ctx, d=d, hq=hq)
     kc = tq.Codec(d, tq.TQ_PROD, 4, w["codec"].flip, w["codec"].S)
@@ -185,6 +199,103 @@ def main():
     }
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(res), flush=True)
+
+
+def bench_layers(a, torch, synth, tq, dev):
+    """Many-layer workloads, all layers resident in HBM; a step is every
+    layer's encode of K and V plus its attention from the fresh codes.
+
+    llama_prefill: 32 layers x 8 KV heads x 131072 tokens x d128 fp16
+      (per-channel stds log-uniform in [0.05, 5], 1% of tokens x10); K prod
+      b=3 (2-bit table + 1-bit QJL), V mse b=3; one decode step of 32 query
+      heads per layer over all 131072 tokens.
+    esm2: 33 layers x batch 64 x 20 heads x 1024 tokens x d64 fp16 (2 heavy
+      channels per head x15); RoPE (base 10000) on K before the rotation and
+      on the queries; K prod b=3, V mse b=3; bidirectional attention of all
+      1024 queries of every head over its 1024 keys."""
+    if a.workload == "llama_prefill":
+        P = synth.llama_prefill_params()
+        L, hkv, d, ctx, hq = 32, P["hkv"], P["d"], P["ctx"], P["hq"]
+        layers = [synth.llama_prefill_layer(P, l, device=dev) for l in range(L)]
+        batch, n_q, heads, rope_k, rope_q = 1, 1, hkv, None, None
+        qs = [x["q"].reshape(1, hq, 1, d) for x in layers]
+        desc = ("llama-prefill: 32 layers x 8 KV heads x 131072 tokens x d128 fp16 (channel stds "
+                "log-uniform [0.05,5], 1% hot tokens x10); K prod b=3 (2+1 QJL), V mse b=3; one "
+                "decode step of 32 query heads per layer")
+    else:
+        P = synth.esm2_params()
+        L, batch, heads, ctx, d = P["layers"], P["batch"], P["heads"], P["seq"], P["d"]
+        layers = [synth.esm2_layer(P, l, device=dev) for l in range(L)]
+        hkv, hq, n_q = heads, heads, ctx
+        rope_k, rope_q = (10000.0, ctx), (10000.0, 0)
+        qs = [x["q"] for x in layers]
+        desc = ("esm2: 33 layers x 64 sequences x 20 heads x 1024 tokens x d64 fp16 (2 heavy "
+                "channels per head x15); RoPE base 10000 on K and q; K prod b=3 (2+1 QJL), "
+                "V mse b=3; bidirectional attention, 1024 x 1024 scores per head")
+    n = batch * heads * ctx                     # vectors per tensor per layer
+    kc = tq.Codec(d, tq.TQ_PROD, 3, P["codec"].flip, P["codec"].S)
+    vc = tq.Codec(d, tq.TQ_MSE, 3, P["codec"].flip)
+    kpk = [tq.Packed(kc, n, dev) for _ in range(L)]
+    vpk = [tq.Packed(vc, n, dev) for _ in range(L)]
+    outs = [torch.empty((batch, hq, n_q, d), dtype=torch.float32, device=dev) for _ in range(L)]
+    ws = torch.zeros((tq.attend_workspace_bytes(batch, n_q, hq, hkv, ctx, d),), dtype=torch.uint8,
+                     device=dev)
+
+    def enc_k(l):
+        tq.encode_kv(kc, None, layers[l]["k"], None, rope=rope_k, kout=kpk[l])
+
+    def enc_v(l):
+        tq.encode_kv(None, vc, None, layers[l]["v"], vout=vpk[l])
+
+    def attend(l):
+        tq.attend_decode(kc, vc, qs[l], kpk[l], vpk[l], ctx, hkv, rope=rope_q, out=outs[l],
+                         workspace=ws)
+
+    for _ in range(a.warmup):
+        for l in range(L):
+            enc_k(l)
+            enc_v(l)
+            attend(l)
+    torch.cuda.synchronize()
+    t = {"encode_k": [], "encode_v": [], "attend": []}
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        for name, fn in (("encode_k", enc_k), ("encode_v", enc_v), ("attend", attend)):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for l in range(L):
+                fn(l)
+            e1.record()
+            torch.cuda.synchronize()
+            t[name].append(e0.elapsed_time(e1) * 1e-3 / L)      # seconds per layer
+    wall = time.perf_counter() - t0
+    tk, tv, ta = (float(np.median(t[x])) for x in ("encode_k", "encode_v", "attend"))
+    # algorithmic bytes per layer: fp16 in + packed out (encode), packed codes read (attention)
+    kout = d * 2 // 8 + d // 8 + 8
+    vout = d * 3 // 8 + 4
+    kbytes, vbytes, abytes = n * (2 * d + kout), n * (2 * d + vout), n * (kout + vout)
+    parts = {"encode_k": (tk, kbytes), "encode_v": (tv, vbytes), "attend": (ta, abytes)}
+    dom = max(parts, key=lambda x: parts[x][0])
+    res = {
+        "metric": "KV vectors encoded/s and decode-attention GB/s over packed codes (% of HBM peak)",
+        "value": 2 * n * L / (wall / a.steps), "unit": "vectors/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": wall / a.steps * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic", "config": {"workload": desc, "layers": L, "vectors_per_step": 2 * n * L},
+        "encode": {"us_k_per_layer": tk * 1e6, "us_v_per_layer": tv * 1e6,
+                   "vectors_per_s": 2 * n / (tk + tv),
+                   "frac_of_hbm_peak": (kbytes + vbytes) / (tk + tv) / 1e9 / HBM_PEAK_GBS},
+        "attend": {"us_per_layer": ta * 1e6, "GB_per_s": abytes / ta / 1e9,
+                   "frac_of_hbm_peak": abytes / ta / 1e9 / HBM_PEAK_GBS},
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": parts[dom][1] / parts[dom][0] / 1e9,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": parts[dom][1] / parts[dom][0] / 1e9 / HBM_PEAK_GBS, "traffic": None},
+    }
+    if a.workload == "esm2":
+        pairs = batch * heads * ctx * ctx
+        res["attend"]["qk_pairs_per_s"] = pairs / ta
     print(json.dumps(res), flush=True)
 
 

@@ -280,6 +280,7 @@ static void plan(int batch, int n_q, int hq, int hkv, int64_t ctx, int& nchunks,
 
 size_t attend_workspace_bytes(int batch, int n_q, int hq, int hkv, int64_t ctx, int d) {
   if (decode_path(n_q, hq, hkv)) return decode_workspace_bytes(batch, n_q, hq, hkv, ctx, d);
+  if (mq_path(n_q, hq, hkv, d)) return mq_workspace_bytes(batch, n_q, hq);
   int nchunks, splits;
   int64_t split_len;
   plan(batch, n_q, hq, hkv, ctx, nchunks, splits, split_len);
@@ -325,6 +326,9 @@ hipError_t launch_attend(const tq_codec& kc, const tq_codec& vc, const void* q, 
   if (decode_path(n_q, hq, hkv))
     return launch_decode(kc, vc, q, q_dtype, batch, n_q, hq, hkv, rope, k, v, ctx, scale, out,
                          scores_out, workspace, stream);
+  if (mq_path(n_q, hq, hkv, kc.d))
+    return launch_attend_mq(kc, vc, q, q_dtype, batch, n_q, hq, hkv, rope, k, v, ctx, scale, out,
+                            scores_out, workspace, stream);
   const int d = kc.d;
   int nchunks, splits;
   int64_t split_len;

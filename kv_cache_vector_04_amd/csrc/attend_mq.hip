@@ -1,0 +1,446 @@
+// Attention from packed codes with many query rows per KV head (the
+// bidirectional protein-model case: every position attends to every
+// position), d = 64.  "TurboESM", "2. Metodologia" part E: unpack, correct
+// and attend with an online softmax in one pass; "Google presenta
+// TurboQuant", "Eliminación del sesgo interno del producto" for the score
+//   s_j = scale nu_j ( <q_rot, c_K[idx_j]> + sqrt(pi/2)/m gamma_j <Sq, 2 sigma_j - 1> ).
+//
+// A workgroup of 4 waves owns 128 query rows of one (batch, KV head) and
+// walks the whole key range in 64-token tiles.  Per tile the codes are
+// dequantized once into LDS and shared by all 128 rows:
+//   K: nu_j scale c_K[idx] as fp16 hi + lo, [token][coordinate];
+//   signs: +-f_j with f_j = nu_j scale sqrt(pi/2)/m gamma_j, as hi + lo;
+//   V: nu^V_j c_V[idx] as hi + lo, transposed to [coordinate][token].
+// Both products run on the matrix cores (v_mfma_f32_32x32x16_f16) with fp32
+// accumulation and the hi / lo splits (hi.hi + hi.lo + lo.hi):
+//   scores, transposed: S^T[token][query] = K q + signs Sq, so that a lane
+//     holds one query's scores for 32 tokens and the softmax reductions stay
+//     in the lane (plus one exchange between lane halves);
+//   values: O^T[coordinate][query] += V^T P^T with the weights P taken
+//     straight from the score registers: the value tile's token columns are
+//     stored in the order that matches the score layout (bits 2 and 3 of
+//     the token index swapped).
+// At the end each lane divides by the softmax sum and applies
+// o = D_V H (O / L) / sqrt(d): butterflies over its 32 coordinates in
+// registers plus one exchange between lane halves.
+
+#include <cmath>
+
+#include "device_common.hpp"
+#include "internal.hpp"
+#include "qprep.hpp"
+
+namespace tqk {
+
+constexpr int kMqWaves = 4;
+constexpr int kMqThreads = kMqWaves * kWave;
+constexpr int kMqRows = 32 * kMqWaves;   // query rows per workgroup
+constexpr int kMqTile = 64;              // tokens per tile
+constexpr int kMqStr = 72;               // halves per LDS row (64 + 8: conflict-free 16-byte reads)
+
+struct MqParams {
+  const uint8_t* kidx;
+  const uint8_t* kqjl;
+  const float* knorm;
+  const float* krnorm;
+  const uint8_t* vidx;
+  const float* vnorm;
+  const float* qrot;     // [rows][64]
+  const float* sq;       // [rows][64]
+  float* out;            // [rows][64]
+  float* scores_out;     // optional [rows][ctx]
+  int64_t ctx;
+  int hq, hkv, n_q, G, nqb;
+  float scale, qjl_scale, inv_sqrt_d;
+  float kcent[16];
+  float vcent[16];
+  uint32_t vflip[2];
+};
+
+typedef uint32_t mq_u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t mq_h16(float x) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
+// hi / lo fp16 pair of one float, as two 16-bit patterns
+__device__ __forceinline__ void mq_split(float x, uint32_t& hi, uint32_t& lo) {
+  const _Float16 h = (_Float16)x;
+  hi = (uint32_t)__builtin_bit_cast(uint16_t, h);
+  lo = mq_h16(x - (float)h);
+}
+
+// value of lane l ^ 32 (the other half of the wave)
+__device__ __forceinline__ float mq_partner(float x, int h) {
+  uint32_t a = __float_as_uint(x), b = a;
+  swap_halves(a, b);
+  return __uint_as_float(h ? a : b);
+}
+
+template <int CBK, int CBV>
+__global__ __launch_bounds__(kMqThreads, 2) void attend_mq_kernel(MqParams p) {
+  constexpr int D = 64;
+  constexpr int KRW = D * CBK / 32;      // words per key row
+  constexpr int VRW = D * CBV / 32;      // words per value row
+  __shared__ __align__(16) _Float16 s_kh[kMqTile][kMqStr];
+  __shared__ __align__(16) _Float16 s_kl[kMqTile][kMqStr];
+  __shared__ __align__(16) _Float16 s_sh[kMqTile][kMqStr];
+  __shared__ __align__(16) _Float16 s_sl[kMqTile][kMqStr];
+  __shared__ __align__(16) _Float16 s_vh[D][kMqStr];
+  __shared__ __align__(16) _Float16 s_vl[D][kMqStr];
+  __shared__ uint32_t s_kraw[kMqTile][KRW];
+  __shared__ uint32_t s_sraw[kMqTile][2];
+  __shared__ uint32_t s_vraw[kMqTile][VRW];
+  __shared__ float s_fk[kMqTile], s_fs[kMqTile], s_nv[kMqTile];
+  __shared__ float s_kc[16], s_vc[16];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int bg = blockIdx.x / p.nqb, qb = blockIdx.x % p.nqb;
+  const int g = bg % p.hkv, b = bg / p.hkv;
+  const int rows = p.G * p.n_q;                              // query rows of this KV head
+  const int r = qb * kMqRows + wave * 32 + l32;              // this lane's query row
+  const bool rok = r < rows;
+  const int64_t row_base = ((int64_t)b * p.hq + (int64_t)g * p.G) * p.n_q;
+  const int64_t kv_base = (int64_t)bg * p.ctx;
+
+  // query fragments (B operand): coordinates 16 ks + 8 h + j of row r
+  mq_u32x4 fq[4][4];     // [k step][q_hi, q_lo, Sq_hi, Sq_lo]
+  {
+    const int64_t row = row_base + (rok ? r : 0);
+#pragma unroll
+    for (int pl = 0; pl < 2; ++pl) {
+      const float* src = (pl ? p.sq : p.qrot) + row * D + 8 * h;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const float4 x0 = reinterpret_cast<const float4*>(src + 16 * ks)[0];
+        const float4 x1 = reinterpret_cast<const float4*>(src + 16 * ks)[1];
+        const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        uint32_t hi[8], lo[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) mq_split(rok ? xs[j] : 0.f, hi[j], lo[j]);
+        fq[ks][2 * pl] = mq_u32x4{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16),
+                                  hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16)};
+        fq[ks][2 * pl + 1] = mq_u32x4{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16),
+                                      lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16)};
+      }
+    }
+  }
+  if (tid < 16) {
+    s_kc[tid] = p.kcent[tid];
+    s_vc[tid] = p.vcent[tid];
+  }
+
+  f32x16 O[2];           // O^T: coordinates 32 cb + 8 (v / 4) + 4 h + v % 4, column = query
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) O[cb][v] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  for (int64_t tile = 0; tile < p.ctx; tile += kMqTile) {
+    __syncthreads();                       // the previous tile's operands are consumed
+    // raw codes and norms of the tile (tokens past the end: zero codes, zero norms)
+    for (int i = tid; i < kMqTile * KRW; i += kMqThreads) {
+      const int tok = i / KRW, w = i % KRW;
+      const int64_t t = tile + tok;
+      s_kraw[tok][w] = t < p.ctx ? reinterpret_cast<const uint32_t*>(p.kidx)[(kv_base + t) * KRW + w] : 0u;
+    }
+    for (int i = tid; i < kMqTile * VRW; i += kMqThreads) {
+      const int tok = i / VRW, w = i % VRW;
+      const int64_t t = tile + tok;
+      s_vraw[tok][w] = t < p.ctx ? reinterpret_cast<const uint32_t*>(p.vidx)[(kv_base + t) * VRW + w] : 0u;
+    }
+    if (tid < 2 * kMqTile) {
+      const int tok = tid >> 1, w = tid & 1;
+      const int64_t t = tile + tok;
+      s_sraw[tok][w] = t < p.ctx ? reinterpret_cast<const uint32_t*>(p.kqjl)[(kv_base + t) * 2 + w] : 0u;
+    } else if (tid < 3 * kMqTile) {
+      const int tok = tid - 2 * kMqTile;
+      const int64_t t = tile + tok;
+      const bool ok = t < p.ctx;
+      const float nk = ok ? p.knorm[kv_base + t] * p.scale : 0.f;
+      s_fk[tok] = nk;
+      s_fs[tok] = ok ? nk * p.krnorm[kv_base + t] * p.qjl_scale : 0.f;
+      s_nv[tok] = ok ? p.vnorm[kv_base + t] : 0.f;
+    }
+    __syncthreads();
+    // dequantize: thread -> (token tid / 4, coordinates 16 (tid % 4) ... + 15) for K and signs
+    {
+      const int tok = tid >> 2, c0 = 16 * (tid & 3);
+      const float fk = s_fk[tok], fs = s_fs[tok];
+      uint32_t kh[8], kl[8];
+#pragma unroll
+      for (int j = 0; j < 16; j += 2) {
+        uint32_t code[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int bit = (c0 + j + e) * CBK;
+          const int w = bit >> 5, sh = bit & 31;
+          uint32_t x = s_kraw[tok][w] >> sh;
+          if (sh + CBK > 32) x |= s_kraw[tok][w + 1] << (32 - sh);
+          code[e] = x & ((1u << CBK) - 1u);
+        }
+        uint32_t h0, l0, h1, l1;
+        mq_split(s_kc[code[0]] * fk, h0, l0);
+        mq_split(s_kc[code[1]] * fk, h1, l1);
+        kh[j >> 1] = h0 | (h1 << 16);
+        kl[j >> 1] = l0 | (l1 << 16);
+      }
+      *reinterpret_cast<mq_u32x4*>(&s_kh[tok][c0]) = mq_u32x4{kh[0], kh[1], kh[2], kh[3]};
+      *reinterpret_cast<mq_u32x4*>(&s_kh[tok][c0 + 8]) = mq_u32x4{kh[4], kh[5], kh[6], kh[7]};
+      *reinterpret_cast<mq_u32x4*>(&s_kl[tok][c0]) = mq_u32x4{kl[0], kl[1], kl[2], kl[3]};
+      *reinterpret_cast<mq_u32x4*>(&s_kl[tok][c0 + 8]) = mq_u32x4{kl[4], kl[5], kl[6], kl[7]};
+      uint32_t fh, fl;
+      mq_split(fs, fh, fl);
+      const uint32_t sb = (s_sraw[tok][c0 >> 5] >> (c0 & 31)) & 0xffffu;
+      uint32_t sh2[8], sl2[8];
+#pragma unroll
+      for (int j = 0; j < 16; j += 2) {
+        const uint32_t n0 = ((sb >> j) & 1u) ? 0u : 0x8000u;        // sign bit of -f
+        const uint32_t n1 = ((sb >> (j + 1)) & 1u) ? 0u : 0x8000u;
+        sh2[j >> 1] = (fh ^ n0) | ((fh ^ n1) << 16);
+        sl2[j >> 1] = (fl ^ n0) | ((fl ^ n1) << 16);
+      }
+      *reinterpret_cast<mq_u32x4*>(&s_sh[tok][c0]) = mq_u32x4{sh2[0], sh2[1], sh2[2], sh2[3]};
+      *reinterpret_cast<mq_u32x4*>(&s_sh[tok][c0 + 8]) = mq_u32x4{sh2[4], sh2[5], sh2[6], sh2[7]};
+      *reinterpret_cast<mq_u32x4*>(&s_sl[tok][c0]) = mq_u32x4{sl2[0], sl2[1], sl2[2], sl2[3]};
+      *reinterpret_cast<mq_u32x4*>(&s_sl[tok][c0 + 8]) = mq_u32x4{sl2[4], sl2[5], sl2[6], sl2[7]};
+    }
+    // values: thread -> (coordinate tid % 64, tokens 16 (tid / 64) ... + 15), column order
+    // with bits 2 and 3 of the token index swapped
+    {
+      const int c = tid & 63, tg = tid >> 6;
+      const int bit = c * CBV, w = bit >> 5, sh = bit & 31;
+      uint32_t vh[8], vl[8];
+#pragma unroll
+      for (int j = 0; j < 16; j += 2) {
+        float val[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int jj = j + e;                                  // column within the 16
+          const int ti = (jj & 3) | ((jj & 4) << 1) | ((jj & 8) >> 1);   // token within the 16
+          const int tok = 16 * tg + ti;
+          uint32_t x = s_vraw[tok][w] >> sh;
+          if (sh + CBV > 32) x |= s_vraw[tok][w + 1] << (32 - sh);
+          val[e] = s_vc[x & ((1u << CBV) - 1u)] * s_nv[tok];
+        }
+        uint32_t h0, l0, h1, l1;
+        mq_split(val[0], h0, l0);
+        mq_split(val[1], h1, l1);
+        vh[j >> 1] = h0 | (h1 << 16);
+        vl[j >> 1] = l0 | (l1 << 16);
+      }
+      *reinterpret_cast<mq_u32x4*>(&s_vh[c][16 * tg]) = mq_u32x4{vh[0], vh[1], vh[2], vh[3]};
+      *reinterpret_cast<mq_u32x4*>(&s_vh[c][16 * tg + 8]) = mq_u32x4{vh[4], vh[5], vh[6], vh[7]};
+      *reinterpret_cast<mq_u32x4*>(&s_vl[c][16 * tg]) = mq_u32x4{vl[0], vl[1], vl[2], vl[3]};
+      *reinterpret_cast<mq_u32x4*>(&s_vl[c][16 * tg + 8]) = mq_u32x4{vl[4], vl[5], vl[6], vl[7]};
+    }
+    __syncthreads();
+
+    // ---- scores, transposed: rows = 32 tokens of block bk, column = query ----
+    f32x16 S[2];
+#pragma unroll
+    for (int bk = 0; bk < 2; ++bk) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) S[bk][v] = 0.f;
+      const int trow = 32 * bk + l32;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int k0 = 16 * ks + 8 * h;
+        const half8_t akh = *reinterpret_cast<const half8_t*>(&s_kh[trow][k0]);
+        const half8_t akl = *reinterpret_cast<const half8_t*>(&s_kl[trow][k0]);
+        const half8_t ash = *reinterpret_cast<const half8_t*>(&s_sh[trow][k0]);
+        const half8_t asl = *reinterpret_cast<const half8_t*>(&s_sl[trow][k0]);
+        const half8_t qh = __builtin_bit_cast(half8_t, fq[ks][0]);
+        const half8_t ql = __builtin_bit_cast(half8_t, fq[ks][1]);
+        const half8_t sqh = __builtin_bit_cast(half8_t, fq[ks][2]);
+        const half8_t sql = __builtin_bit_cast(half8_t, fq[ks][3]);
+        S[bk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(akh, qh, S[bk], 0, 0, 0);
+        S[bk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(akh, ql, S[bk], 0, 0, 0);
+        S[bk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(akl, qh, S[bk], 0, 0, 0);
+        S[bk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ash, sqh, S[bk], 0, 0, 0);
+        S[bk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ash, sql, S[bk], 0, 0, 0);
+        S[bk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(asl, sqh, S[bk], 0, 0, 0);
+      }
+    }
+    // token of S[bk][v]: tile + 32 bk + 8 (v / 4) + 4 h + v % 4
+    float mt = -INFINITY;
+#pragma unroll
+    for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t t = tile + 32 * bk + 8 * (v >> 2) + 4 * h + (v & 3);
+        if (t >= p.ctx) S[bk][v] = -INFINITY;
+        mt = fmaxf(mt, S[bk][v]);
+      }
+    if (p.scores_out != nullptr && rok) {
+#pragma unroll
+      for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int64_t t = tile + 32 * bk + 8 * (v >> 2) + 4 * h + (v & 3);
+          if (t < p.ctx) p.scores_out[(row_base + r) * p.ctx + t] = S[bk][v];
+        }
+    }
+    mt = fmaxf(mt, mq_partner(mt, h));
+    const float mn = fmaxf(m_run, mt);                 // finite: the tile has a valid token
+    const float alpha = __expf(m_run - mn);            // 0 on the first tile
+    m_run = mn;
+    float ls = 0.f;
+#pragma unroll
+    for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        S[bk][v] = __expf(S[bk][v] - mn);
+        ls += S[bk][v];
+      }
+    l_run = fmaf(l_run, alpha, ls);
+    if (alpha != 1.f) {
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) O[cb][v] *= alpha;
+    }
+
+    // ---- values: O^T += V^T P^T, 16 tokens per product ----
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int bk = ks >> 1, v0 = 8 * (ks & 1);
+      uint32_t ph[4], pl[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t h0, l0, h1, l1;
+        mq_split(S[bk][v0 + 2 * j], h0, l0);
+        mq_split(S[bk][v0 + 2 * j + 1], h1, l1);
+        ph[j] = h0 | (h1 << 16);
+        pl[j] = l0 | (l1 << 16);
+      }
+      const half8_t bph = __builtin_bit_cast(half8_t, mq_u32x4{ph[0], ph[1], ph[2], ph[3]});
+      const half8_t bpl = __builtin_bit_cast(half8_t, mq_u32x4{pl[0], pl[1], pl[2], pl[3]});
+      const int col = 32 * bk + 16 * (ks & 1) + 8 * h;
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const half8_t avh = *reinterpret_cast<const half8_t*>(&s_vh[32 * cb + l32][col]);
+        const half8_t avl = *reinterpret_cast<const half8_t*>(&s_vl[32 * cb + l32][col]);
+        O[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(avh, bph, O[cb], 0, 0, 0);
+        O[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(avh, bpl, O[cb], 0, 0, 0);
+        O[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(avl, bph, O[cb], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- o = D_V H (O / L) / sqrt(d) for this lane's query ----
+  const float L = l_run + mq_partner(l_run, h);
+  const float inv = 1.f / L;
+  float x[2][16];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) x[cb][v] = O[cb][v] * inv;
+  // coordinate bits: 0, 1 = v & 3; 2 = h; 3, 4 = v >> 2; 5 = cb
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) {       // v bits (coordinate bits 0, 1, 3, 4)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        if ((v & m) == 0) {
+          const float a = x[cb][v], c = x[cb][v | m];
+          x[cb][v] = a + c;
+          x[cb][v | m] = a - c;
+        }
+  }
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {           // cb (coordinate bit 5)
+    const float a = x[0][v], c = x[1][v];
+    x[0][v] = a + c;
+    x[1][v] = a - c;
+  }
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)           // h (coordinate bit 2), across lane halves
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const float o = mq_partner(x[cb][v], h);
+      x[cb][v] = h ? (o - x[cb][v]) : (x[cb][v] + o);
+    }
+  if (rok) {
+    float* dst = p.out + (row_base + r) * D;
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4) {
+        const int i0 = 32 * cb + 8 * v4 + 4 * h;
+        float o4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = i0 + e;
+          const uint32_t bit = (p.vflip[i >> 5] >> (i & 31)) & 1u;
+          const float o = x[cb][4 * v4 + e] * p.inv_sqrt_d;
+          o4[e] = bit ? -o : o;
+        }
+        *reinterpret_cast<float4*>(dst + i0) = make_float4(o4[0], o4[1], o4[2], o4[3]);
+      }
+  }
+}
+
+bool mq_path(int n_q, int hq, int hkv, int d) {
+  return d == 64 && !decode_path(n_q, hq, hkv);
+}
+
+size_t mq_workspace_bytes(int batch, int n_q, int hq) {
+  const size_t rows = (size_t)batch * hq * n_q;
+  return rows * 64 * 2 * sizeof(float);
+}
+
+template <int CBK, int CBV>
+static hipError_t run_mq(const MqParams& p, unsigned blocks, hipStream_t s) {
+  hipLaunchKernelGGL((attend_mq_kernel<CBK, CBV>), dim3(blocks), dim3(kMqThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int CBK>
+static hipError_t mq_pick_v(int cbv, const MqParams& p, unsigned blocks, hipStream_t s) {
+  switch (cbv) {
+    case 1: return run_mq<CBK, 1>(p, blocks, s);
+    case 2: return run_mq<CBK, 2>(p, blocks, s);
+    case 3: return run_mq<CBK, 3>(p, blocks, s);
+    case 4: return run_mq<CBK, 4>(p, blocks, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_attend_mq(const tq_codec& kc, const tq_codec& vc, const void* q, int q_dtype,
+                            int batch, int n_q, int hq, int hkv, const RopeHost& rope,
+                            const tq_packed& k, const tq_packed& v, int64_t ctx, float scale,
+                            float* out, float* scores_out, void* workspace, hipStream_t stream) {
+  constexpr int D = 64;
+  if (kc.d != D) return hipErrorInvalidValue;
+  const int64_t rows = (int64_t)batch * hq * n_q;
+  float* qrot = reinterpret_cast<float*>(workspace);
+  float* sq = qrot + (size_t)rows * D;
+  hipError_t e = launch_qprep(kc, q, q_dtype, rows, n_q, rope, qrot, sq, stream);
+  if (e != hipSuccess) return e;
+  MqParams p = {};
+  p.kidx = k.idx; p.kqjl = k.qjl; p.knorm = k.norm; p.krnorm = k.rnorm;
+  p.vidx = v.idx; p.vnorm = v.norm;
+  p.qrot = qrot; p.sq = sq; p.out = out; p.scores_out = scores_out;
+  p.ctx = ctx; p.hq = hq; p.hkv = hkv; p.n_q = n_q; p.G = hq / hkv;
+  p.nqb = (p.G * n_q + kMqRows - 1) / kMqRows;
+  p.scale = scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)D));
+  p.qjl_scale = (float)(std::sqrt(M_PI / 2.0) / kc.m);
+  p.inv_sqrt_d = (float)(1.0 / std::sqrt((double)D));
+  for (int i = 0; i < 16; ++i) { p.kcent[i] = kc.centroids[i]; p.vcent[i] = vc.centroids[i]; }
+  p.vflip[0] = vc.flip[0];
+  p.vflip[1] = vc.flip[1];
+  const unsigned blocks = (unsigned)((int64_t)batch * hkv * p.nqb);
+  switch (kc.code_bits) {
+    case 1: return mq_pick_v<1>(vc.code_bits, p, blocks, stream);
+    case 2: return mq_pick_v<2>(vc.code_bits, p, blocks, stream);
+    case 3: return mq_pick_v<3>(vc.code_bits, p, blocks, stream);
+    case 4: return mq_pick_v<4>(vc.code_bits, p, blocks, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace tqk

@@ -41,6 +41,13 @@ hipError_t launch_attend(const tq_codec& kc, const tq_codec& vc, const void* q,
                          hipStream_t stream);
 
 bool decode_path(int n_q, int hq, int hkv);
+// many query rows per KV head at d = 64 (attend_mq.hip)
+bool mq_path(int n_q, int hq, int hkv, int d);
+size_t mq_workspace_bytes(int batch, int n_q, int hq);
+hipError_t launch_attend_mq(const tq_codec& kc, const tq_codec& vc, const void* q, int q_dtype,
+                            int batch, int n_q, int hq, int hkv, const RopeHost& rope,
+                            const tq_packed& k, const tq_packed& v, int64_t ctx, float scale,
+                            float* out, float* scores_out, void* workspace, hipStream_t stream);
 size_t decode_workspace_bytes(int batch, int n_q, int hq, int hkv, int64_t ctx, int d);
 hipError_t launch_decode(const tq_codec& kc, const tq_codec& vc, const void* q, int q_dtype,
                          int batch, int n_q, int hq, int hkv, const RopeHost& rope,
