@@ -32,8 +32,12 @@
 
 namespace tqk {
 
-constexpr int kDecWaves = 12;
-constexpr int kDecThreads = kDecWaves * kWave;
+// Waves per workgroup: 12 (3 per SIMD).
+template <int CBV>
+struct DecWaves {
+  static constexpr int kWaves = 12;
+  static constexpr int kThreads = kWaves * kWave;
+};
 constexpr int kDecRows = 4;
 
 struct DecodeParams {
@@ -141,6 +145,8 @@ struct DecGeom {
   // LDS carve-up (bytes)
   static constexpr int LK_B = NF * NE * 16;
   static constexpr int LQ_B = NB * 256 * 16;
+  static constexpr int kDecWaves = DecWaves<CBV>::kWaves;
+  static constexpr int kDecThreads = DecWaves<CBV>::kThreads;
   static constexpr int MRG_B = kDecWaves * kDecRows * (D + 2) * 4;   // wave merge
   static constexpr int SQP_B = kDecThreads * 16;                      // Sq partials
   static constexpr int TAB0_B = (LK_B + LQ_B) > SQP_B ? (LK_B + LQ_B) : SQP_B;
@@ -160,7 +166,9 @@ struct TileRegs {
 };
 
 template <int D, int CBK, int CBV>
-__global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeParams p) {
+__global__ __launch_bounds__(DecWaves<CBV>::kThreads) void decode_kernel(DecodeParams p) {
+  constexpr int kDecWaves = DecWaves<CBV>::kWaves;
+  constexpr int kDecThreads = DecWaves<CBV>::kThreads;
   using Gm = DecGeom<D, CBK, CBV>;
   using KG = typename Gm::KG;
   constexpr int NF = Gm::NF, NE = Gm::NE, NB = Gm::NB, WK = Gm::WK, KROW = Gm::KROW;
@@ -178,6 +186,14 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeParams p) {
   __shared__ float s_kc[16], s_vc[16];
   __shared__ uint32_t s_kflip[D / 32];
   __shared__ double s_theta[D / 2];
+  // 3-bit value codes: the lane groups' 24 bits straddle words, so each
+  // wave stages its tile's value rows here instead of holding two words per
+  // token in registers
+  // (where LDS allows: the 64 KB key table of 1- and 3-bit keys at d = 128
+  // leaves no room, and those variants keep the two-word registers)
+  constexpr bool VST = CBV == 3 && (D == 64 || CBK % 2 == 0);
+  constexpr int VSTR = VW + 1;
+  __shared__ uint32_t s_vst[VST ? kDecWaves * kWave * VSTR : 1];
 
   float4* s_lk = reinterpret_cast<float4*>(s_tab);
   float4* s_lq = reinterpret_cast<float4*>(s_tab + Gm::LK_B);
@@ -376,13 +392,19 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeParams p) {
     const bool valid = tok < t1;
     // this tile's value codes (used after the scores)
     uint32_t vwr[TPL][2];
+    uint32_t vrow[VST ? VW : 1];   // 3-bit codes: the lane's own token row, staged to LDS
+    if constexpr (VST) {
+      const int64_t vt = valid ? tok : t0;
+      load_words<VW, (VROW % 16 == 0) ? 16 : 8>(p.vidx + (kv_base + vt) * VROW, vrow);
+    } else {
 #pragma unroll
-    for (int u = 0; u < TPL; ++u) {
-      int64_t vt = tile + (int64_t)u * TS + ts;
-      vt = vt < t1 ? vt : t0;
-      const uint32_t* vr = reinterpret_cast<const uint32_t*>(p.vidx + (kv_base + vt) * VROW);
-      vwr[u][0] = vr[vw0];
-      vwr[u][1] = vstraddle ? vr[vw1] : 0u;
+      for (int u = 0; u < TPL; ++u) {
+        int64_t vt = tile + (int64_t)u * TS + ts;
+        vt = vt < t1 ? vt : t0;
+        const uint32_t* vr = reinterpret_cast<const uint32_t*>(p.vidx + (kv_base + vt) * VROW);
+        vwr[u][0] = vr[vw0];
+        vwr[u][1] = vstraddle ? vr[vw1] : 0u;
+      }
     }
 
     // four independent accumulation chains per table
@@ -428,15 +450,24 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeParams p) {
       for (int k = 0; k < 8; ++k) acc[r][k] *= alpha;
     }
     s_w[wave * kWave + lane] = make_float4(pw[0], pw[1], pw[2], pw[3]);
-    // LDS operations of one wave complete in order: the weights written
-    // above are visible to the reads below without a workgroup barrier.
+    if constexpr (VST) {
+#pragma unroll
+      for (int w = 0; w < VW; ++w) s_vst[(wave * kWave + lane) * VSTR + w] = vrow[w];
+    }
+    // LDS operations of one wave complete in order: the weights (and rows)
+    // written above are visible to the reads below without a workgroup barrier.
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int u = 0; u < TPL; ++u) {
       const float4 w = s_w[wave * kWave + u * TS + ts];
-      const uint32_t bits = vstraddle
-                                ? __builtin_amdgcn_alignbit(vwr[u][1], vwr[u][0], vbit0 & 31)
-                                : (vwr[u][0] >> (vbit0 & 31));
+      uint32_t bits;
+      if constexpr (VST) {
+        const uint32_t* vr = s_vst + (wave * kWave + u * TS + ts) * VSTR;
+        bits = __builtin_amdgcn_alignbit(vr[vw1], vr[vw0], vbit0 & 31);
+      } else {
+        bits = vstraddle ? __builtin_amdgcn_alignbit(vwr[u][1], vwr[u][0], vbit0 & 31)
+                         : (vwr[u][0] >> (vbit0 & 31));
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint32_t pv = (bits >> (2 * CBV * e)) & (NVE - 1);
@@ -609,7 +640,7 @@ size_t decode_workspace_bytes(int batch, int n_q, int hq, int hkv, int64_t ctx, 
 
 template <int D, int CBK, int CBV>
 static hipError_t run_decode(const DecodeParams& p, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((decode_kernel<D, CBK, CBV>), grid, dim3(kDecThreads), 0, s, p);
+  hipLaunchKernelGGL((decode_kernel<D, CBK, CBV>), grid, dim3(DecWaves<CBV>::kThreads), 0, s, p);
   return hipGetLastError();
 }
 
