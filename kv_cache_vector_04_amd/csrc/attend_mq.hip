@@ -5,9 +5,9 @@
 // TurboQuant", "Eliminación del sesgo interno del producto" for the score
 //   s_j = scale nu_j ( <q_rot, c_K[idx_j]> + sqrt(pi/2)/m gamma_j <Sq, 2 sigma_j - 1> ).
 //
-// A workgroup of 4 waves owns 128 query rows of one (batch, KV head) and
+// A workgroup of 8 waves owns 256 query rows of one (batch, KV head) and
 // walks the whole key range in 64-token tiles.  Per tile the codes are
-// dequantized once into LDS and shared by all 128 rows:
+// dequantized once into LDS and shared by all 256 rows:
 //   K: nu_j scale c_K[idx] as fp16 hi + lo, [token][coordinate];
 //   signs: +-f_j with f_j = nu_j scale sqrt(pi/2)/m gamma_j, as hi + lo;
 //   V: nu^V_j c_V[idx] as hi + lo, transposed to [coordinate][token].
@@ -32,7 +32,7 @@
 
 namespace tqk {
 
-constexpr int kMqWaves = 4;
+constexpr int kMqWaves = 8;
 constexpr int kMqThreads = kMqWaves * kWave;
 constexpr int kMqRows = 32 * kMqWaves;   // query rows per workgroup
 constexpr int kMqTile = 64;              // tokens per tile
@@ -82,6 +82,9 @@ __global__ __launch_bounds__(kMqThreads, 2) void attend_mq_kernel(MqParams p) {
   constexpr int D = 64;
   constexpr int KRW = D * CBK / 32;      // words per key row
   constexpr int VRW = D * CBV / 32;      // words per value row
+  constexpr int CPT = kMqTile * D / kMqThreads;   // key coordinates dequantized per thread
+  constexpr int TPT = kMqTile * D / kMqThreads;   // value tokens dequantized per thread
+  static_assert(CPT % 8 == 0 && CPT <= 16 && TPT % 8 == 0, "16-byte LDS stores");
   __shared__ __align__(16) _Float16 s_kh[kMqTile][kMqStr];
   __shared__ __align__(16) _Float16 s_kl[kMqTile][kMqStr];
   __shared__ __align__(16) _Float16 s_sh[kMqTile][kMqStr];
@@ -138,40 +141,72 @@ __global__ __launch_bounds__(kMqThreads, 2) void attend_mq_kernel(MqParams p) {
     for (int v = 0; v < 16; ++v) O[cb][v] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  for (int64_t tile = 0; tile < p.ctx; tile += kMqTile) {
-    __syncthreads();                       // the previous tile's operands are consumed
-    // raw codes and norms of the tile (tokens past the end: zero codes, zero norms)
-    for (int i = tid; i < kMqTile * KRW; i += kMqThreads) {
+  // raw codes and norms of a tile, loaded into registers one tile ahead
+  // (tokens past the end: zero codes, zero norms)
+  constexpr int KPT = (kMqTile * KRW + kMqThreads - 1) / kMqThreads;   // key words per thread
+  constexpr int VPT = (kMqTile * VRW + kMqThreads - 1) / kMqThreads;   // value words per thread
+  uint32_t rk[KPT], rv[VPT], rs = 0u;
+  float rn0 = 0.f, rn1 = 0.f, rn2 = 0.f;
+  auto load_raw = [&](int64_t tile) {
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const int i = tid + u * kMqThreads;
       const int tok = i / KRW, w = i % KRW;
       const int64_t t = tile + tok;
-      s_kraw[tok][w] = t < p.ctx ? reinterpret_cast<const uint32_t*>(p.kidx)[(kv_base + t) * KRW + w] : 0u;
+      rk[u] = (i < kMqTile * KRW && t < p.ctx)
+                  ? reinterpret_cast<const uint32_t*>(p.kidx)[(kv_base + t) * KRW + w] : 0u;
     }
-    for (int i = tid; i < kMqTile * VRW; i += kMqThreads) {
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+      const int i = tid + u * kMqThreads;
       const int tok = i / VRW, w = i % VRW;
       const int64_t t = tile + tok;
-      s_vraw[tok][w] = t < p.ctx ? reinterpret_cast<const uint32_t*>(p.vidx)[(kv_base + t) * VRW + w] : 0u;
+      rv[u] = (i < kMqTile * VRW && t < p.ctx)
+                  ? reinterpret_cast<const uint32_t*>(p.vidx)[(kv_base + t) * VRW + w] : 0u;
     }
     if (tid < 2 * kMqTile) {
-      const int tok = tid >> 1, w = tid & 1;
-      const int64_t t = tile + tok;
-      s_sraw[tok][w] = t < p.ctx ? reinterpret_cast<const uint32_t*>(p.kqjl)[(kv_base + t) * 2 + w] : 0u;
+      const int64_t t = tile + (tid >> 1);
+      rs = t < p.ctx ? reinterpret_cast<const uint32_t*>(p.kqjl)[(kv_base + t) * 2 + (tid & 1)] : 0u;
+    } else if (tid < 3 * kMqTile) {
+      const int64_t t = tile + (tid - 2 * kMqTile);
+      const bool ok = t < p.ctx;
+      rn0 = ok ? p.knorm[kv_base + t] : 0.f;
+      rn1 = ok ? p.krnorm[kv_base + t] : 0.f;
+      rn2 = ok ? p.vnorm[kv_base + t] : 0.f;
+    }
+  };
+  load_raw(0);
+
+  for (int64_t tile = 0; tile < p.ctx; tile += kMqTile) {
+    __syncthreads();                       // the previous tile's operands are consumed
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const int i = tid + u * kMqThreads;
+      if (i < kMqTile * KRW) s_kraw[i / KRW][i % KRW] = rk[u];
+    }
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+      const int i = tid + u * kMqThreads;
+      if (i < kMqTile * VRW) s_vraw[i / VRW][i % VRW] = rv[u];
+    }
+    if (tid < 2 * kMqTile) {
+      s_sraw[tid >> 1][tid & 1] = rs;
     } else if (tid < 3 * kMqTile) {
       const int tok = tid - 2 * kMqTile;
-      const int64_t t = tile + tok;
-      const bool ok = t < p.ctx;
-      const float nk = ok ? p.knorm[kv_base + t] * p.scale : 0.f;
+      const float nk = rn0 * p.scale;
       s_fk[tok] = nk;
-      s_fs[tok] = ok ? nk * p.krnorm[kv_base + t] * p.qjl_scale : 0.f;
-      s_nv[tok] = ok ? p.vnorm[kv_base + t] : 0.f;
+      s_fs[tok] = nk * rn1 * p.qjl_scale;
+      s_nv[tok] = rn2;
     }
     __syncthreads();
-    // dequantize: thread -> (token tid / 4, coordinates 16 (tid % 4) ... + 15) for K and signs
+    if (tile + kMqTile < p.ctx) load_raw(tile + kMqTile);
+    // dequantize: thread -> (token, CPT coordinates) for K and signs
     {
-      const int tok = tid >> 2, c0 = 16 * (tid & 3);
+      const int tok = tid / (kMqTile / CPT), c0 = CPT * (tid % (kMqTile / CPT));
       const float fk = s_fk[tok], fs = s_fs[tok];
-      uint32_t kh[8], kl[8];
+      uint32_t kh[CPT / 2], kl[CPT / 2];
 #pragma unroll
-      for (int j = 0; j < 16; j += 2) {
+      for (int j = 0; j < CPT; j += 2) {
         uint32_t code[2];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
@@ -187,40 +222,42 @@ __global__ __launch_bounds__(kMqThreads, 2) void attend_mq_kernel(MqParams p) {
         kh[j >> 1] = h0 | (h1 << 16);
         kl[j >> 1] = l0 | (l1 << 16);
       }
-      *reinterpret_cast<mq_u32x4*>(&s_kh[tok][c0]) = mq_u32x4{kh[0], kh[1], kh[2], kh[3]};
-      *reinterpret_cast<mq_u32x4*>(&s_kh[tok][c0 + 8]) = mq_u32x4{kh[4], kh[5], kh[6], kh[7]};
-      *reinterpret_cast<mq_u32x4*>(&s_kl[tok][c0]) = mq_u32x4{kl[0], kl[1], kl[2], kl[3]};
-      *reinterpret_cast<mq_u32x4*>(&s_kl[tok][c0 + 8]) = mq_u32x4{kl[4], kl[5], kl[6], kl[7]};
       uint32_t fh, fl;
       mq_split(fs, fh, fl);
-      const uint32_t sb = (s_sraw[tok][c0 >> 5] >> (c0 & 31)) & 0xffffu;
-      uint32_t sh2[8], sl2[8];
+      const uint32_t sb = (s_sraw[tok][c0 >> 5] >> (c0 & 31)) & ((1u << CPT) - 1u);
+      uint32_t sh2[CPT / 2], sl2[CPT / 2];
 #pragma unroll
-      for (int j = 0; j < 16; j += 2) {
+      for (int j = 0; j < CPT; j += 2) {
         const uint32_t n0 = ((sb >> j) & 1u) ? 0u : 0x8000u;        // sign bit of -f
         const uint32_t n1 = ((sb >> (j + 1)) & 1u) ? 0u : 0x8000u;
         sh2[j >> 1] = (fh ^ n0) | ((fh ^ n1) << 16);
         sl2[j >> 1] = (fl ^ n0) | ((fl ^ n1) << 16);
       }
-      *reinterpret_cast<mq_u32x4*>(&s_sh[tok][c0]) = mq_u32x4{sh2[0], sh2[1], sh2[2], sh2[3]};
-      *reinterpret_cast<mq_u32x4*>(&s_sh[tok][c0 + 8]) = mq_u32x4{sh2[4], sh2[5], sh2[6], sh2[7]};
-      *reinterpret_cast<mq_u32x4*>(&s_sl[tok][c0]) = mq_u32x4{sl2[0], sl2[1], sl2[2], sl2[3]};
-      *reinterpret_cast<mq_u32x4*>(&s_sl[tok][c0 + 8]) = mq_u32x4{sl2[4], sl2[5], sl2[6], sl2[7]};
-    }
-    // values: thread -> (coordinate tid % 64, tokens 16 (tid / 64) ... + 15), column order
-    // with bits 2 and 3 of the token index swapped
-    {
-      const int c = tid & 63, tg = tid >> 6;
-      const int bit = c * CBV, w = bit >> 5, sh = bit & 31;
-      uint32_t vh[8], vl[8];
 #pragma unroll
-      for (int j = 0; j < 16; j += 2) {
+      for (int q4 = 0; q4 < CPT / 8; ++q4) {
+        *reinterpret_cast<mq_u32x4*>(&s_kh[tok][c0 + 8 * q4]) =
+            mq_u32x4{kh[4 * q4], kh[4 * q4 + 1], kh[4 * q4 + 2], kh[4 * q4 + 3]};
+        *reinterpret_cast<mq_u32x4*>(&s_kl[tok][c0 + 8 * q4]) =
+            mq_u32x4{kl[4 * q4], kl[4 * q4 + 1], kl[4 * q4 + 2], kl[4 * q4 + 3]};
+        *reinterpret_cast<mq_u32x4*>(&s_sh[tok][c0 + 8 * q4]) =
+            mq_u32x4{sh2[4 * q4], sh2[4 * q4 + 1], sh2[4 * q4 + 2], sh2[4 * q4 + 3]};
+        *reinterpret_cast<mq_u32x4*>(&s_sl[tok][c0 + 8 * q4]) =
+            mq_u32x4{sl2[4 * q4], sl2[4 * q4 + 1], sl2[4 * q4 + 2], sl2[4 * q4 + 3]};
+      }
+    }
+    // values: thread -> (coordinate tid % 64, columns TPT (tid / 64) ... + TPT - 1);
+    // column col holds token col with bits 2 and 3 swapped
+    {
+      const int c = tid & 63, col0 = TPT * (tid >> 6);
+      const int bit = c * CBV, w = bit >> 5, sh = bit & 31;
+      uint32_t vh[TPT / 2], vl[TPT / 2];
+#pragma unroll
+      for (int j = 0; j < TPT; j += 2) {
         float val[2];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          const int jj = j + e;                                  // column within the 16
-          const int ti = (jj & 3) | ((jj & 4) << 1) | ((jj & 8) >> 1);   // token within the 16
-          const int tok = 16 * tg + ti;
+          const int col = col0 + j + e;
+          const int tok = (col & ~12) | ((col & 4) << 1) | ((col & 8) >> 1);
           uint32_t x = s_vraw[tok][w] >> sh;
           if (sh + CBV > 32) x |= s_vraw[tok][w + 1] << (32 - sh);
           val[e] = s_vc[x & ((1u << CBV) - 1u)] * s_nv[tok];
@@ -231,10 +268,13 @@ __global__ __launch_bounds__(kMqThreads, 2) void attend_mq_kernel(MqParams p) {
         vh[j >> 1] = h0 | (h1 << 16);
         vl[j >> 1] = l0 | (l1 << 16);
       }
-      *reinterpret_cast<mq_u32x4*>(&s_vh[c][16 * tg]) = mq_u32x4{vh[0], vh[1], vh[2], vh[3]};
-      *reinterpret_cast<mq_u32x4*>(&s_vh[c][16 * tg + 8]) = mq_u32x4{vh[4], vh[5], vh[6], vh[7]};
-      *reinterpret_cast<mq_u32x4*>(&s_vl[c][16 * tg]) = mq_u32x4{vl[0], vl[1], vl[2], vl[3]};
-      *reinterpret_cast<mq_u32x4*>(&s_vl[c][16 * tg + 8]) = mq_u32x4{vl[4], vl[5], vl[6], vl[7]};
+#pragma unroll
+      for (int q4 = 0; q4 < TPT / 8; ++q4) {
+        *reinterpret_cast<mq_u32x4*>(&s_vh[c][col0 + 8 * q4]) =
+            mq_u32x4{vh[4 * q4], vh[4 * q4 + 1], vh[4 * q4 + 2], vh[4 * q4 + 3]};
+        *reinterpret_cast<mq_u32x4*>(&s_vl[c][col0 + 8 * q4]) =
+            mq_u32x4{vl[4 * q4], vl[4 * q4 + 1], vl[4 * q4 + 2], vl[4 * q4 + 3]};
+      }
     }
     __syncthreads();
 

@@ -4,10 +4,12 @@
 // estimate of <q, x> is linear in q ("Google presenta TurboQuant ...",
 // "Eliminación del sesgo interno del producto").
 //
-// A workgroup prepares kQRows query rows: their butterflies run through
-// LDS, and S is staged once into LDS with a padded row stride (d + 1
-// floats, so that the lanes of a wave reading S[i][k] for consecutive i hit
-// distinct banks) and read from there for the d-long dot products.
+// A workgroup prepares QR query rows (8, or 64 when there are many rows, so
+// that S is staged and the butterfly barriers are paid once per 64 rows):
+// their butterflies run through LDS, and S is staged once into LDS with a
+// padded row stride (d + 1 floats, so that the lanes of a wave reading
+// S[i][k] for consecutive i hit distinct banks) and read from there for the
+// d-long dot products.
 
 #include <cmath>
 
@@ -17,10 +19,9 @@
 
 namespace tqk {
 
-constexpr int kQRows = 8;
 constexpr int kQThreads = 256;
 
-template <int D, typename T, bool ROPE>
+template <int D, typename T, bool ROPE, int kQRows>
 __global__ __launch_bounds__(kQThreads) void qprep_kernel(QPrepParams p) {
   constexpr int SP = D + 1;                         // padded S row stride
   __shared__ float s_S[D * SP];
@@ -122,14 +123,20 @@ __global__ __launch_bounds__(kQThreads) void qprep_kernel(QPrepParams p) {
   }
 }
 
+template <int D, typename T, int QR>
+static hipError_t run_qprep_rows(const QPrepParams& p, bool rope, hipStream_t s) {
+  const unsigned blocks = (unsigned)((p.n_rows + QR - 1) / QR);
+  if (rope)
+    hipLaunchKernelGGL((qprep_kernel<D, T, true, QR>), dim3(blocks), dim3(kQThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL((qprep_kernel<D, T, false, QR>), dim3(blocks), dim3(kQThreads), 0, s, p);
+  return hipGetLastError();
+}
+
 template <int D, typename T>
 static hipError_t run_qprep(const QPrepParams& p, bool rope, hipStream_t s) {
-  const unsigned blocks = (unsigned)((p.n_rows + kQRows - 1) / kQRows);
-  if (rope)
-    hipLaunchKernelGGL((qprep_kernel<D, T, true>), dim3(blocks), dim3(kQThreads), 0, s, p);
-  else
-    hipLaunchKernelGGL((qprep_kernel<D, T, false>), dim3(blocks), dim3(kQThreads), 0, s, p);
-  return hipGetLastError();
+  if (p.n_rows >= 8192) return run_qprep_rows<D, T, 64>(p, rope, s);
+  return run_qprep_rows<D, T, 8>(p, rope, s);
 }
 
 hipError_t launch_qprep(const tq_codec& c, const void* q, int q_dtype, int64_t n_rows,
