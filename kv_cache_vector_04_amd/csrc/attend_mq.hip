@@ -45,8 +45,11 @@ struct MqParams {
   const float* krnorm;
   const uint8_t* vidx;
   const float* vnorm;
-  const float* qrot;     // [rows][64]
-  const float* sq;       // [rows][64]
+  const void* q;         // [rows][64], fp16 or fp32
+  int q_f16;
+  int rope;
+  int32_t pos0;
+  const float* S;        // 64 x 64 row-major
   float* out;            // [rows][64]
   float* scores_out;     // optional [rows][ctx]
   int64_t ctx;
@@ -55,6 +58,8 @@ struct MqParams {
   float kcent[16];
   float vcent[16];
   uint32_t vflip[2];
+  uint32_t kflip[2];
+  double theta[32];      // RoPE: base^(-2i/64)
 };
 
 typedef uint32_t mq_u32x4 __attribute__((ext_vector_type(4)));
@@ -107,26 +112,146 @@ __global__ __launch_bounds__(kMqThreads, 2) void attend_mq_kernel(MqParams p) {
   const int64_t row_base = ((int64_t)b * p.hq + (int64_t)g * p.G) * p.n_q;
   const int64_t kv_base = (int64_t)bg * p.ctx;
 
-  // query fragments (B operand): coordinates 16 ks + 8 h + j of row r
+  // ---- query preparation, in registers: lane (row r, h) holds coordinates
+  // 16 ks + 8 h + j (the B-operand layout of the products below) ----
+  // S as fp16 hi / lo in the key-tile buffers (free until the first tile)
+  for (int i = tid; i < D * D / 4; i += kMqThreads) {
+    const float4 v = reinterpret_cast<const float4*>(p.S)[i];
+    const int row = (4 * i) / D, col = (4 * i) % D;
+    uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
+    mq_split(v.x, h0, l0);
+    mq_split(v.y, h1, l1);
+    mq_split(v.z, h2, l2);
+    mq_split(v.w, h3, l3);
+    *reinterpret_cast<uint2*>(&s_kh[row][col]) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+    *reinterpret_cast<uint2*>(&s_kl[row][col]) = make_uint2(l0 | (l1 << 16), l2 | (l3 << 16));
+  }
   mq_u32x4 fq[4][4];     // [k step][q_hi, q_lo, Sq_hi, Sq_lo]
   {
+    float x[4][8];
     const int64_t row = row_base + (rok ? r : 0);
 #pragma unroll
-    for (int pl = 0; pl < 2; ++pl) {
-      const float* src = (pl ? p.sq : p.qrot) + row * D + 8 * h;
+    for (int ks = 0; ks < 4; ++ks) {
+      const int c0 = 16 * ks + 8 * h;
+      if (p.q_f16) {
+        const uint4 u = *reinterpret_cast<const uint4*>(reinterpret_cast<const _Float16*>(p.q) + row * D + c0);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[ks][2 * e] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[e] & 0xffffu));
+          x[ks][2 * e + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[e] >> 16));
+        }
+      } else {
+        const float4 x0 = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p.q) + row * D + c0)[0];
+        const float4 x1 = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p.q) + row * D + c0)[1];
+        x[ks][0] = x0.x; x[ks][1] = x0.y; x[ks][2] = x0.z; x[ks][3] = x0.w;
+        x[ks][4] = x1.x; x[ks][5] = x1.y; x[ks][6] = x1.z; x[ks][7] = x1.w;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[ks][j] = rok ? x[ks][j] : 0.f;
+      // RoPE on the interleaved pairs (c, c + 1), c even, at position pos0 + r % n_q
+      if (p.rope) {
+        const int64_t pos = (int64_t)p.pos0 + (r % p.n_q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float sn, cs;
+          sincos_reduced((double)pos * p.theta[(c0 >> 1) + e], sn, cs);
+          const float a = x[ks][2 * e], bq = x[ks][2 * e + 1];
+          x[ks][2 * e] = a * cs - bq * sn;
+          x[ks][2 * e + 1] = a * sn + bq * cs;
+        }
+      }
+      // sign flip D_K
+      const uint32_t fw = p.kflip[c0 >> 5] >> (c0 & 31);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        x[ks][j] = __uint_as_float(__float_as_uint(x[ks][j]) ^ (((fw >> j) & 1u) << 31));
+    }
+    // H_64: coordinate bits 0-2 = j, 3 = h (across lane halves), 4-5 = ks
+#pragma unroll
+    for (int m = 1; m < 8; m <<= 1)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if ((j & m) == 0) {
+            const float a = x[ks][j], c = x[ks][j | m];
+            x[ks][j] = a + c;
+            x[ks][j | m] = a - c;
+          }
+#pragma unroll
+    for (int m = 1; m < 4; m <<= 1)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        if ((ks & m) == 0)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float a = x[ks][j], c = x[ks | m][j];
+            x[ks][j] = a + c;
+            x[ks | m][j] = a - c;
+          }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float o = mq_partner(x[ks][j], h);
+        x[ks][j] = (h ? (o - x[ks][j]) : (x[ks][j] + o)) * p.inv_sqrt_d;
+      }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      uint32_t hi[8], lo[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) mq_split(x[ks][j], hi[j], lo[j]);
+      fq[ks][0] = mq_u32x4{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16),
+                           hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16)};
+      fq[ks][1] = mq_u32x4{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16),
+                           lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16)};
+    }
+  }
+  __syncthreads();       // S in LDS
+  {
+    // Sq^T = S q_rot: rows = output coordinates 32 bi + 8 (v / 4) + 4 h + v % 4
+    f32x16 C[2];
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) C[bi][v] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const float4 x0 = reinterpret_cast<const float4*>(src + 16 * ks)[0];
-        const float4 x1 = reinterpret_cast<const float4*>(src + 16 * ks)[1];
-        const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-        uint32_t hi[8], lo[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) mq_split(rok ? xs[j] : 0.f, hi[j], lo[j]);
-        fq[ks][2 * pl] = mq_u32x4{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16),
-                                  hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16)};
-        fq[ks][2 * pl + 1] = mq_u32x4{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16),
-                                      lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16)};
+        const half8_t ah = *reinterpret_cast<const half8_t*>(&s_kh[32 * bi + l32][16 * ks + 8 * h]);
+        const half8_t al = *reinterpret_cast<const half8_t*>(&s_kl[32 * bi + l32][16 * ks + 8 * h]);
+        const half8_t qh = __builtin_bit_cast(half8_t, fq[ks][0]);
+        const half8_t ql = __builtin_bit_cast(half8_t, fq[ks][1]);
+        C[bi] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, qh, C[bi], 0, 0, 0);
+        C[bi] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, ql, C[bi], 0, 0, 0);
+        C[bi] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, qh, C[bi], 0, 0, 0);
       }
+    }
+    // Exchange coordinate bit 2 (the lane half of C) with bit 3 (the lane
+    // half of the operand layout): one half swap per register pair
+    // (v, v + 4), v % 8 < 4.  After it, lane half h holds coordinates with
+    // bit 3 = h: element j = 4 e + (v % 4) of k step 2 bi + v / 8 comes from
+    // register v + 4 e of the pair.
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        if ((v & 4) == 0) {
+          uint32_t a = __float_as_uint(C[bi][v]), c = __float_as_uint(C[bi][v + 4]);
+          swap_halves(a, c);
+          C[bi][v] = __uint_as_float(a);
+          C[bi][v + 4] = __uint_as_float(c);
+        }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int bi = ks >> 1, v0 = 8 * (ks & 1);
+      uint32_t hi[8], lo[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) mq_split(C[bi][v0 + 4 * (j >> 2) + (j & 3)], hi[j], lo[j]);
+      fq[ks][2] = mq_u32x4{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16),
+                           hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16)};
+      fq[ks][3] = mq_u32x4{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16),
+                           lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16)};
     }
   }
   if (tid < 16) {
@@ -429,8 +554,8 @@ bool mq_path(int n_q, int hq, int hkv, int d) {
 }
 
 size_t mq_workspace_bytes(int batch, int n_q, int hq) {
-  const size_t rows = (size_t)batch * hq * n_q;
-  return rows * 64 * 2 * sizeof(float);
+  (void)batch; (void)n_q; (void)hq;
+  return 0;      // the query preparation runs inside the kernel
 }
 
 template <int CBK, int CBV>
@@ -455,16 +580,21 @@ hipError_t launch_attend_mq(const tq_codec& kc, const tq_codec& vc, const void* 
                             const tq_packed& k, const tq_packed& v, int64_t ctx, float scale,
                             float* out, float* scores_out, void* workspace, hipStream_t stream) {
   constexpr int D = 64;
+  (void)workspace;
   if (kc.d != D) return hipErrorInvalidValue;
-  const int64_t rows = (int64_t)batch * hq * n_q;
-  float* qrot = reinterpret_cast<float*>(workspace);
-  float* sq = qrot + (size_t)rows * D;
-  hipError_t e = launch_qprep(kc, q, q_dtype, rows, n_q, rope, qrot, sq, stream);
-  if (e != hipSuccess) return e;
   MqParams p = {};
   p.kidx = k.idx; p.kqjl = k.qjl; p.knorm = k.norm; p.krnorm = k.rnorm;
   p.vidx = v.idx; p.vnorm = v.norm;
-  p.qrot = qrot; p.sq = sq; p.out = out; p.scores_out = scores_out;
+  p.q = q;
+  p.q_f16 = q_dtype == TQ_F16;
+  p.rope = rope.on ? 1 : 0;
+  p.pos0 = rope.on ? rope.pos0 : 0;
+  for (int i = 0; i < D / 2; ++i)
+    p.theta[i] = rope.on ? std::pow((double)rope.base, -2.0 * i / (double)D) : 0.0;
+  p.S = kc.S;
+  p.kflip[0] = kc.flip[0];
+  p.kflip[1] = kc.flip[1];
+  p.out = out; p.scores_out = scores_out;
   p.ctx = ctx; p.hq = hq; p.hkv = hkv; p.n_q = n_q; p.G = hq / hkv;
   p.nqb = (p.G * n_q + kMqRows - 1) / kMqRows;
   p.scale = scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)D));
