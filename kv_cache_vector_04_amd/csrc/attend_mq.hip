@@ -90,16 +90,18 @@ __global__ __launch_bounds__(kMqThreads, 2) void attend_mq_kernel(MqParams p) {
   constexpr int CPT = kMqTile * D / kMqThreads;   // key coordinates dequantized per thread
   constexpr int TPT = kMqTile * D / kMqThreads;   // value tokens dequantized per thread
   static_assert(CPT % 8 == 0 && CPT <= 16 && TPT % 8 == 0, "16-byte LDS stores");
-  __shared__ __align__(16) _Float16 s_kh[kMqTile][kMqStr];
-  __shared__ __align__(16) _Float16 s_kl[kMqTile][kMqStr];
-  __shared__ __align__(16) _Float16 s_sh[kMqTile][kMqStr];
-  __shared__ __align__(16) _Float16 s_sl[kMqTile][kMqStr];
-  __shared__ __align__(16) _Float16 s_vh[D][kMqStr];
-  __shared__ __align__(16) _Float16 s_vl[D][kMqStr];
-  __shared__ uint32_t s_kraw[kMqTile][KRW];
-  __shared__ uint32_t s_sraw[kMqTile][2];
-  __shared__ uint32_t s_vraw[kMqTile][VRW];
-  __shared__ float s_fk[kMqTile], s_fs[kMqTile], s_nv[kMqTile];
+  // two buffers of each: the products of tile i read one while tile i + 1
+  // is dequantized into the other
+  __shared__ __align__(16) _Float16 s_kh[2][kMqTile][kMqStr];
+  __shared__ __align__(16) _Float16 s_kl[2][kMqTile][kMqStr];
+  __shared__ __align__(16) _Float16 s_sh[2][kMqTile][kMqStr];
+  __shared__ __align__(16) _Float16 s_sl[2][kMqTile][kMqStr];
+  __shared__ __align__(16) _Float16 s_vh[2][D][kMqStr];
+  __shared__ __align__(16) _Float16 s_vl[2][D][kMqStr];
+  __shared__ uint32_t s_kraw[2][kMqTile][KRW];
+  __shared__ uint32_t s_sraw[2][kMqTile][2];
+  __shared__ uint32_t s_vraw[2][kMqTile][VRW];
+  __shared__ float s_fk[2][kMqTile], s_fs[2][kMqTile], s_nv[2][kMqTile];
   __shared__ float s_kc[16], s_vc[16];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -114,7 +116,7 @@ __global__ __launch_bounds__(kMqThreads, 2) void attend_mq_kernel(MqParams p) {
 
   // ---- query preparation, in registers: lane (row r, h) holds coordinates
   // 16 ks + 8 h + j (the B-operand layout of the products below) ----
-  // S as fp16 hi / lo in the key-tile buffers (free until the first tile)
+  // S as fp16 hi / lo in key-tile buffer 1 (free until the second tile)
   for (int i = tid; i < D * D / 4; i += kMqThreads) {
     const float4 v = reinterpret_cast<const float4*>(p.S)[i];
     const int row = (4 * i) / D, col = (4 * i) % D;
@@ -123,8 +125,8 @@ __global__ __launch_bounds__(kMqThreads, 2) void attend_mq_kernel(MqParams p) {
     mq_split(v.y, h1, l1);
     mq_split(v.z, h2, l2);
     mq_split(v.w, h3, l3);
-    *reinterpret_cast<uint2*>(&s_kh[row][col]) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
-    *reinterpret_cast<uint2*>(&s_kl[row][col]) = make_uint2(l0 | (l1 << 16), l2 | (l3 << 16));
+    *reinterpret_cast<uint2*>(&s_kh[1][row][col]) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+    *reinterpret_cast<uint2*>(&s_kl[1][row][col]) = make_uint2(l0 | (l1 << 16), l2 | (l3 << 16));
   }
   mq_u32x4 fq[4][4];     // [k step][q_hi, q_lo, Sq_hi, Sq_lo]
   {
@@ -218,8 +220,8 @@ __global__ __launch_bounds__(kMqThreads, 2) void attend_mq_kernel(MqParams p) {
       for (int v = 0; v < 16; ++v) C[bi][v] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const half8_t ah = *reinterpret_cast<const half8_t*>(&s_kh[32 * bi + l32][16 * ks + 8 * h]);
-        const half8_t al = *reinterpret_cast<const half8_t*>(&s_kl[32 * bi + l32][16 * ks + 8 * h]);
+        const half8_t ah = *reinterpret_cast<const half8_t*>(&s_kh[1][32 * bi + l32][16 * ks + 8 * h]);
+        const half8_t al = *reinterpret_cast<const half8_t*>(&s_kl[1][32 * bi + l32][16 * ks + 8 * h]);
         const half8_t qh = __builtin_bit_cast(half8_t, fq[ks][0]);
         const half8_t ql = __builtin_bit_cast(half8_t, fq[ks][1]);
         C[bi] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, qh, C[bi], 0, 0, 0);
@@ -300,35 +302,33 @@ __global__ __launch_bounds__(kMqThreads, 2) void attend_mq_kernel(MqParams p) {
       rn2 = ok ? p.vnorm[kv_base + t] : 0.f;
     }
   };
-  load_raw(0);
-
-  for (int64_t tile = 0; tile < p.ctx; tile += kMqTile) {
-    __syncthreads();                       // the previous tile's operands are consumed
+  // raw tile data lives in slot t % 2 and tile t's operands in buffer t % 2
+  auto store_raw = [&](int rb) {
 #pragma unroll
     for (int u = 0; u < KPT; ++u) {
       const int i = tid + u * kMqThreads;
-      if (i < kMqTile * KRW) s_kraw[i / KRW][i % KRW] = rk[u];
+      if (i < kMqTile * KRW) s_kraw[rb][i / KRW][i % KRW] = rk[u];
     }
 #pragma unroll
     for (int u = 0; u < VPT; ++u) {
       const int i = tid + u * kMqThreads;
-      if (i < kMqTile * VRW) s_vraw[i / VRW][i % VRW] = rv[u];
+      if (i < kMqTile * VRW) s_vraw[rb][i / VRW][i % VRW] = rv[u];
     }
     if (tid < 2 * kMqTile) {
-      s_sraw[tid >> 1][tid & 1] = rs;
+      s_sraw[rb][tid >> 1][tid & 1] = rs;
     } else if (tid < 3 * kMqTile) {
       const int tok = tid - 2 * kMqTile;
       const float nk = rn0 * p.scale;
-      s_fk[tok] = nk;
-      s_fs[tok] = nk * rn1 * p.qjl_scale;
-      s_nv[tok] = rn2;
+      s_fk[rb][tok] = nk;
+      s_fs[rb][tok] = nk * rn1 * p.qjl_scale;
+      s_nv[rb][tok] = rn2;
     }
-    __syncthreads();
-    if (tile + kMqTile < p.ctx) load_raw(tile + kMqTile);
+  };
+  auto dequant = [&](int rb) {
     // dequantize: thread -> (token, CPT coordinates) for K and signs
     {
       const int tok = tid / (kMqTile / CPT), c0 = CPT * (tid % (kMqTile / CPT));
-      const float fk = s_fk[tok], fs = s_fs[tok];
+      const float fk = s_fk[rb][tok], fs = s_fs[rb][tok];
       uint32_t kh[CPT / 2], kl[CPT / 2];
 #pragma unroll
       for (int j = 0; j < CPT; j += 2) {
@@ -337,8 +337,8 @@ __global__ __launch_bounds__(kMqThreads, 2) void attend_mq_kernel(MqParams p) {
         for (int e = 0; e < 2; ++e) {
           const int bit = (c0 + j + e) * CBK;
           const int w = bit >> 5, sh = bit & 31;
-          uint32_t x = s_kraw[tok][w] >> sh;
-          if (sh + CBK > 32) x |= s_kraw[tok][w + 1] << (32 - sh);
+          uint32_t x = s_kraw[rb][tok][w] >> sh;
+          if (sh + CBK > 32) x |= s_kraw[rb][tok][w + 1] << (32 - sh);
           code[e] = x & ((1u << CBK) - 1u);
         }
         uint32_t h0, l0, h1, l1;
@@ -349,7 +349,7 @@ __global__ __launch_bounds__(kMqThreads, 2) void attend_mq_kernel(MqParams p) {
       }
       uint32_t fh, fl;
       mq_split(fs, fh, fl);
-      const uint32_t sb = (s_sraw[tok][c0 >> 5] >> (c0 & 31)) & ((1u << CPT) - 1u);
+      const uint32_t sb = (s_sraw[rb][tok][c0 >> 5] >> (c0 & 31)) & ((1u << CPT) - 1u);
       uint32_t sh2[CPT / 2], sl2[CPT / 2];
 #pragma unroll
       for (int j = 0; j < CPT; j += 2) {
@@ -360,13 +360,13 @@ __global__ __launch_bounds__(kMqThreads, 2) void attend_mq_kernel(MqParams p) {
       }
 #pragma unroll
       for (int q4 = 0; q4 < CPT / 8; ++q4) {
-        *reinterpret_cast<mq_u32x4*>(&s_kh[tok][c0 + 8 * q4]) =
+        *reinterpret_cast<mq_u32x4*>(&s_kh[rb][tok][c0 + 8 * q4]) =
             mq_u32x4{kh[4 * q4], kh[4 * q4 + 1], kh[4 * q4 + 2], kh[4 * q4 + 3]};
-        *reinterpret_cast<mq_u32x4*>(&s_kl[tok][c0 + 8 * q4]) =
+        *reinterpret_cast<mq_u32x4*>(&s_kl[rb][tok][c0 + 8 * q4]) =
             mq_u32x4{kl[4 * q4], kl[4 * q4 + 1], kl[4 * q4 + 2], kl[4 * q4 + 3]};
-        *reinterpret_cast<mq_u32x4*>(&s_sh[tok][c0 + 8 * q4]) =
+        *reinterpret_cast<mq_u32x4*>(&s_sh[rb][tok][c0 + 8 * q4]) =
             mq_u32x4{sh2[4 * q4], sh2[4 * q4 + 1], sh2[4 * q4 + 2], sh2[4 * q4 + 3]};
-        *reinterpret_cast<mq_u32x4*>(&s_sl[tok][c0 + 8 * q4]) =
+        *reinterpret_cast<mq_u32x4*>(&s_sl[rb][tok][c0 + 8 * q4]) =
             mq_u32x4{sl2[4 * q4], sl2[4 * q4 + 1], sl2[4 * q4 + 2], sl2[4 * q4 + 3]};
       }
     }
@@ -383,9 +383,9 @@ __global__ __launch_bounds__(kMqThreads, 2) void attend_mq_kernel(MqParams p) {
         for (int e = 0; e < 2; ++e) {
           const int col = col0 + j + e;
           const int tok = (col & ~12) | ((col & 4) << 1) | ((col & 8) >> 1);
-          uint32_t x = s_vraw[tok][w] >> sh;
-          if (sh + CBV > 32) x |= s_vraw[tok][w + 1] << (32 - sh);
-          val[e] = s_vc[x & ((1u << CBV) - 1u)] * s_nv[tok];
+          uint32_t x = s_vraw[rb][tok][w] >> sh;
+          if (sh + CBV > 32) x |= s_vraw[rb][tok][w + 1] << (32 - sh);
+          val[e] = s_vc[x & ((1u << CBV) - 1u)] * s_nv[rb][tok];
         }
         uint32_t h0, l0, h1, l1;
         mq_split(val[0], h0, l0);
@@ -395,14 +395,29 @@ __global__ __launch_bounds__(kMqThreads, 2) void attend_mq_kernel(MqParams p) {
       }
 #pragma unroll
       for (int q4 = 0; q4 < TPT / 8; ++q4) {
-        *reinterpret_cast<mq_u32x4*>(&s_vh[c][col0 + 8 * q4]) =
+        *reinterpret_cast<mq_u32x4*>(&s_vh[rb][c][col0 + 8 * q4]) =
             mq_u32x4{vh[4 * q4], vh[4 * q4 + 1], vh[4 * q4 + 2], vh[4 * q4 + 3]};
-        *reinterpret_cast<mq_u32x4*>(&s_vl[c][col0 + 8 * q4]) =
+        *reinterpret_cast<mq_u32x4*>(&s_vl[rb][c][col0 + 8 * q4]) =
             mq_u32x4{vl[4 * q4], vl[4 * q4 + 1], vl[4 * q4 + 2], vl[4 * q4 + 3]};
       }
     }
-    __syncthreads();
+  };
+  load_raw(0);
+  store_raw(0);
+  if (kMqTile < p.ctx) load_raw(kMqTile);
+  __syncthreads();
+  dequant(0);
+  if (kMqTile < p.ctx) store_raw(1);
+  if (2 * kMqTile < p.ctx) load_raw(2 * kMqTile);
+  __syncthreads();
 
+  int cur = 0;
+  for (int64_t tile = 0; tile < p.ctx; tile += kMqTile, cur ^= 1) {
+    // the next tile's operands, beside this tile's products
+    if (tile + kMqTile < p.ctx) dequant(cur ^ 1);
+    // tile + 2 into the raw slot the previous dequantization freed, tile + 3 in flight
+    if (tile + 2 * kMqTile < p.ctx) store_raw(cur);
+    if (tile + 3 * kMqTile < p.ctx) load_raw(tile + 3 * kMqTile);
     // ---- scores, transposed: rows = 32 tokens of block bk, column = query ----
     f32x16 S[2];
 #pragma unroll
@@ -413,10 +428,10 @@ __global__ __launch_bounds__(kMqThreads, 2) void attend_mq_kernel(MqParams p) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const int k0 = 16 * ks + 8 * h;
-        const half8_t akh = *reinterpret_cast<const half8_t*>(&s_kh[trow][k0]);
-        const half8_t akl = *reinterpret_cast<const half8_t*>(&s_kl[trow][k0]);
-        const half8_t ash = *reinterpret_cast<const half8_t*>(&s_sh[trow][k0]);
-        const half8_t asl = *reinterpret_cast<const half8_t*>(&s_sl[trow][k0]);
+        const half8_t akh = *reinterpret_cast<const half8_t*>(&s_kh[cur][trow][k0]);
+        const half8_t akl = *reinterpret_cast<const half8_t*>(&s_kl[cur][trow][k0]);
+        const half8_t ash = *reinterpret_cast<const half8_t*>(&s_sh[cur][trow][k0]);
+        const half8_t asl = *reinterpret_cast<const half8_t*>(&s_sl[cur][trow][k0]);
         const half8_t qh = __builtin_bit_cast(half8_t, fq[ks][0]);
         const half8_t ql = __builtin_bit_cast(half8_t, fq[ks][1]);
         const half8_t sqh = __builtin_bit_cast(half8_t, fq[ks][2]);
@@ -486,13 +501,14 @@ __global__ __launch_bounds__(kMqThreads, 2) void attend_mq_kernel(MqParams p) {
       const int col = 32 * bk + 16 * (ks & 1) + 8 * h;
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
-        const half8_t avh = *reinterpret_cast<const half8_t*>(&s_vh[32 * cb + l32][col]);
-        const half8_t avl = *reinterpret_cast<const half8_t*>(&s_vl[32 * cb + l32][col]);
+        const half8_t avh = *reinterpret_cast<const half8_t*>(&s_vh[cur][32 * cb + l32][col]);
+        const half8_t avl = *reinterpret_cast<const half8_t*>(&s_vl[cur][32 * cb + l32][col]);
         O[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(avh, bph, O[cb], 0, 0, 0);
         O[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(avh, bpl, O[cb], 0, 0, 0);
         O[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(avl, bph, O[cb], 0, 0, 0);
       }
     }
+    __syncthreads();     // buffer cur^1 written, buffer cur and raw slot cur^1 read
   }
 
   // ---- o = D_V H (O / L) / sqrt(d) for this lane's query ----
