@@ -108,6 +108,8 @@ extern "C" int tq_encode_kv(const tq_codec* kc, const tq_codec* vc, const void* 
   if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256)))
     return TQ_ERR_WORKSPACE;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (kc != nullptr && vc != nullptr && tqk::encode_kv_fusable(*kc, *vc, dtype, rope != nullptr))
+    return hip_status(tqk::launch_encode_kv(*kc, *vc, k, v, n_rows, *kout, *vout, hs));
   for (int s = 0; s < 2; ++s) {
     if (cs[s] == nullptr) continue;
     const tqk::RopeHost rh = s == 0 ? rope_of(rope) : tqk::RopeHost{};

@@ -420,35 +420,38 @@ __device__ __forceinline__ float cross_sum(float v) {
   return __uint_as_float(a) + __uint_as_float(b);
 }
 
-template <int D, int CB, bool PROD>
-__global__ __launch_bounds__(HalfLaunch<PROD>::kWaves * kWave, HalfLaunch<PROD>::kMinWavesPerEU) void encode_half_kernel(EncodeParams p) {
-  constexpr int kHalfWaves = HalfLaunch<PROD>::kWaves;
+// LDS tables of one codec for the two-lanes-per-vector encoder
+template <int D, int CB, bool PROD, bool MROT = false>
+struct HalfTables {
+  static constexpr int FRAGS = (D / 32) * (D / 16);
+  float cent[16];
+  float2 lut[CB >= 3 ? kLutMax : 1];
+  uint4 hmask[MROT ? 1 : D / 8];
+  uint4 hd[MROT ? FRAGS * kWave : 1];   // H D as A fragments (rotation on the matrix cores)
+  uint4 frag[PROD ? FRAGS * 2 * kWave : 1];
+};
+
+// The tables from the codec (all nthr threads of the workgroup take part;
+// the caller synchronizes afterwards).  kp: p in the kernel argument
+// segment, for indexing its arrays with run-time indices.
+template <int D, int CB, bool PROD, bool MROT = false>
+__device__ __forceinline__ void half_setup(const EncodeParams& p, const EncodeParams* kp,
+                                           HalfTables<D, CB, PROD, MROT>& T, int tid, int nthr) {
   constexpr int NLEV = 1 << CB;
   constexpr int NTH = NLEV - 1;
-  constexpr int HALF = D / 2;              // coordinates per lane
-  constexpr int NP = D / 4;                // packed fp16 pairs per lane
-  constexpr int HW = HALF * CB / 32;       // code words per lane (half a row)
-  constexpr int ROW_BYTES = D * CB / 8;
-  constexpr int HB = ROW_BYTES / 2;
-  constexpr int HALIGN = HB % 16 == 0 ? 16 : (HB % 8 == 0 ? 8 : 4);
+  constexpr int HALF = D / 2;
+  constexpr int NP = D / 4;
   constexpr bool USE_LUT = CB >= 3;
   constexpr int KS = D / 16, MT = D / 32, FRAGS = MT * KS;
-
-  __shared__ float s_cent[16];
-  __shared__ float2 s_lut[USE_LUT ? kLutMax : 1];
-  __shared__ uint4 s_hmask[NP / 2];
-  __shared__ uint4 s_frag[PROD ? FRAGS * 2 * kWave : 1];
-
-  const int tid = threadIdx.x;
-  const EncodeParams* kp = (const EncodeParams*)__builtin_amdgcn_kernarg_segment_ptr();
+  (void)MT;
   const float cscale = PROD ? 256.f : 1.f;
-  if (tid < 16) s_cent[tid] = kp->codec.centroids[tid] * cscale;
-  if (tid >= 64 && tid < 64 + NP / 2)
-    s_hmask[tid - 64] = make_uint4(kp->hflip[4 * (tid - 64)], kp->hflip[4 * (tid - 64) + 1],
+  if (tid < 16) T.cent[tid] = kp->codec.centroids[tid] * cscale;
+  if (!MROT && tid >= 64 && tid < 64 + NP / 2)
+    T.hmask[tid - 64] = make_uint4(kp->hflip[4 * (tid - 64)], kp->hflip[4 * (tid - 64) + 1],
                                    kp->hflip[4 * (tid - 64) + 2], kp->hflip[4 * (tid - 64) + 3]);
   if constexpr (USE_LUT) {
     const float a = p.lut_a, b = p.lut_b;
-    for (int g = tid; g < p.lut_g; g += blockDim.x) {
+    for (int g = tid; g < p.lut_g; g += nthr) {
       int base = 0;
       float thr = INFINITY;
 #pragma unroll
@@ -458,13 +461,13 @@ __global__ __launch_bounds__(HalfLaunch<PROD>::kWaves * kWave, HalfLaunch<PROD>:
         base += cell < g ? 1 : 0;
         if (cell == g) thr = tu;
       }
-      s_lut[g] = make_float2(thr, __int_as_float(base));
+      T.lut[g] = make_float2(thr, __int_as_float(base));
     }
   }
   if constexpr (PROD) {
     // fragment (mt, ks), lane l: row 32 mt + perm(l%32) of S (perm as in the
     // one-vector-per-lane kernel), columns (l/32) d/2 + 8 ks + 0..7
-    for (int t = tid; t < FRAGS * kWave; t += blockDim.x) {
+    for (int t = tid; t < FRAGS * kWave; t += nthr) {
       const int lane = t & 63, f = t >> 6;
       const int mt = f / KS, ks = f % KS;
       const int rho = lane & 31;
@@ -480,43 +483,83 @@ __global__ __launch_bounds__(HalfLaunch<PROD>::kWaves * kWave, HalfLaunch<PROD>:
         hi[j] = (_Float16)sv[j];
         lo[j] = (_Float16)(sv[j] - (float)hi[j]);
       }
-      s_frag[(2 * f) * kWave + lane] =
+      T.frag[(2 * f) * kWave + lane] =
           make_uint4(pack_h2(hi[0], hi[1]), pack_h2(hi[2], hi[3]), pack_h2(hi[4], hi[5]), pack_h2(hi[6], hi[7]));
-      s_frag[(2 * f + 1) * kWave + lane] =
+      T.frag[(2 * f + 1) * kWave + lane] =
           make_uint4(pack_h2(lo[0], lo[1]), pack_h2(lo[2], lo[3]), pack_h2(lo[4], lo[5]), pack_h2(lo[6], lo[7]));
     }
   }
-  __syncthreads();
+  if constexpr (MROT) {
+    // fragment (mt, ks), lane l: row sigma(mt, l%32) = (d/2) ((l/4)%2) +
+    // 16 mt + 4 ((l%32)/8) + l%4 of H D, columns (d/2) (l/32) + 8 ks + 0..7.
+    // With that row order, register v of the product's tile mt lands, in
+    // lane half h, on coordinate (d/2) h + 16 mt + v: the input's layout.
+    for (int t = tid; t < FRAGS * kWave; t += nthr) {
+      const int lane = t & 63, f = t >> 6;
+      const int mt = f / KS, ks = f % KS;
+      const int rho = lane & 31;
+      const int sig = HALF * ((rho >> 2) & 1) + 16 * mt + 4 * (rho >> 3) + (rho & 3);
+      uint32_t w[4];
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        uint32_t e[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int pi = HALF * (lane >> 5) + 8 * ks + j + q;
+          const uint32_t neg = ((uint32_t)__popc(sig & pi) + (kp->codec.flip[pi >> 5] >> (pi & 31))) & 1u;
+          e[q] = neg ? 0xBC00u : 0x3C00u;   // fp16 -1 / +1
+        }
+        w[j >> 1] = e[0] | (e[1] << 16);
+      }
+      T.hd[t] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
 
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
+// Loads the input of tile t for this lane (rows past the end read as zeros).
+template <int D>
+__device__ __forceinline__ void half_load(const EncodeParams& p, int64_t t, uint32_t (&dst)[D / 4]) {
+  constexpr int NP = D / 4;
+  const int lane = threadIdx.x & 63, h = lane >> 5;
+  const int64_t r = t * 32 + (lane & 31);
+  if (t < (p.n_rows + 31) / 32 && r < p.n_rows) {
+    const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const _Float16*>(p.x) + r * D + h * (D / 2));
+#pragma unroll
+    for (int j = 0; j < NP / 4; ++j) {
+      const uint4 v = src[j];
+      dst[4 * j] = v.x; dst[4 * j + 1] = v.y; dst[4 * j + 2] = v.z; dst[4 * j + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < NP; ++j) dst[j] = 0u;
+  }
+}
+
+// One wave's tiles: tile, tile + tstride, ...  With PF the input of the
+// next tile is loaded while the current one is processed, and nxt holds
+// the first tile's input on entry.
+template <int D, int CB, bool PROD, bool PF, bool MROT = false>
+__device__ __forceinline__ void half_tiles(const EncodeParams& p, const HalfTables<D, CB, PROD, MROT>& T,
+                                           int64_t tile, int64_t tstride, uint32_t (&nxt)[D / 4]) {
+  constexpr int NLEV = 1 << CB;
+  constexpr int NTH = NLEV - 1;
+  constexpr int HALF = D / 2;              // coordinates per lane
+  constexpr int NP = D / 4;                // packed fp16 pairs per lane
+  constexpr int HW = HALF * CB / 32;       // code words per lane (half a row)
+  constexpr int ROW_BYTES = D * CB / 8;
+  constexpr int HB = ROW_BYTES / 2;
+  constexpr int HALIGN = HB % 16 == 0 ? 16 : (HB % 8 == 0 ? 8 : 4);
+  constexpr bool USE_LUT = CB >= 3;
+  constexpr int KS = D / 16, MT = D / 32;
+  (void)NTH;
+  const int lane = threadIdx.x & 63;
   const int h = lane >> 5;
   const float sgn = h ? -1.f : 1.f;
   const int64_t ntiles = (p.n_rows + 31) / 32;
   const _Float16* __restrict__ xin = reinterpret_cast<const _Float16*>(p.x);
   const float lut_a = p.lut_a, lut_b = p.lut_b;
-
-  // the input of the wave's next tile is loaded while the current one is
-  // processed (rows past the end read as zeros and are not stored)
-  auto load_tile = [&](int64_t t, uint32_t (&dst)[NP]) {
-    const int64_t r = t * 32 + (lane & 31);
-    if (t < ntiles && r < p.n_rows) {
-      const uint4* src = reinterpret_cast<const uint4*>(xin + r * D + h * HALF);
-#pragma unroll
-      for (int j = 0; j < NP / 4; ++j) {
-        const uint4 v = src[j];
-        dst[4 * j] = v.x; dst[4 * j + 1] = v.y; dst[4 * j + 2] = v.z; dst[4 * j + 3] = v.w;
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < NP; ++j) dst[j] = 0u;
-    }
-  };
-  const int64_t tstride = (int64_t)gridDim.x * kHalfWaves;
-  int64_t tile = (int64_t)blockIdx.x * kHalfWaves + wave;
-  constexpr bool PF = HalfLaunch<PROD>::kPrefetch;
-  uint32_t nxt[NP];
-  if (PF) load_tile(tile, nxt);
+  const float cscale = PROD ? 256.f : 1.f;
+  auto load_tile = [&](int64_t t, uint32_t (&dst)[NP]) { half_load<D>(p, t, dst); };
   for (; tile < ntiles; tile += tstride) {
     const int64_t row = tile * 32 + (lane & 31);
     const bool valid = row < p.n_rows;
@@ -556,33 +599,58 @@ __global__ __launch_bounds__(HalfLaunch<PROD>::kWaves * kWave, HalfLaunch<PROD>:
     }
     const float nu_s = sqrtf(nu2);
 
-    // sign flip, the stage across the halves, and the stage on bit 0
     float x[HALF];
+    if constexpr (MROT) {
+      // y = H D x on the matrix cores: B = the lane's own input (k slot j of
+      // lane half h at step ks is coordinate (d/2) h + 8 ks + j), A = the
+      // H D fragments; fp16 input times +-1 is exact, sums in fp32
+      f32x16 acc_y[MT];
 #pragma unroll
-    for (int j4 = 0; j4 < NP / 4; ++j4) {
-      const uint4 m4 = s_hmask[h * (NP / 4) + j4];
-      const uint32_t ms[4] = {m4.x, m4.y, m4.z, m4.w};
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = 4 * j4 + e;
-        uint32_t a = u[j] ^ ms[e], b = a;
-        swap_halves(a, b);   // a: the low lane's pair, b: the high lane's pair
-        float t0, t1;
-        asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,0,0] op_sel_hi:[1,0,1]" : "=v"(t0) : "v"(b), "v"(sgn), "v"(a));
-        asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,1] op_sel_hi:[1,0,1]" : "=v"(t1) : "v"(b), "v"(sgn), "v"(a));
-        x[2 * j] = t0 + t1;
-        x[2 * j + 1] = t0 - t1;
+        for (int v = 0; v < 16; ++v) acc_y[mt][v] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const half8_t bx = __builtin_bit_cast(half8_t, make_uint4(u[4 * ks], u[4 * ks + 1], u[4 * ks + 2], u[4 * ks + 3]));
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const half8_t ahd = __builtin_bit_cast(half8_t, T.hd[(mt * KS + ks) * kWave + lane]);
+          acc_y[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahd, bx, acc_y[mt], 0, 0, 0);
+        }
       }
-    }
-    if (PF) load_tile(tile + tstride, nxt);
+      if (PF) load_tile(tile + tstride, nxt);
 #pragma unroll
-    for (int hh = 2; hh < HALF; hh <<= 1) {
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int i = 0; i < HALF; ++i) {
-        if ((i & hh) == 0) {
-          const float a = x[i], b = x[i + hh];
-          x[i] = a + b;
-          x[i + hh] = a - b;
+        for (int v = 0; v < 16; ++v) x[16 * mt + v] = acc_y[mt][v];
+    } else {
+      // sign flip, the stage across the halves, and the stage on bit 0
+#pragma unroll
+      for (int j4 = 0; j4 < NP / 4; ++j4) {
+        const uint4 m4 = T.hmask[h * (NP / 4) + j4];
+        const uint32_t ms[4] = {m4.x, m4.y, m4.z, m4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = 4 * j4 + e;
+          uint32_t a = u[j] ^ ms[e], b = a;
+          swap_halves(a, b);   // a: the low lane's pair, b: the high lane's pair
+          float t0, t1;
+          asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,0,0] op_sel_hi:[1,0,1]" : "=v"(t0) : "v"(b), "v"(sgn), "v"(a));
+          asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,1] op_sel_hi:[1,0,1]" : "=v"(t1) : "v"(b), "v"(sgn), "v"(a));
+          x[2 * j] = t0 + t1;
+          x[2 * j + 1] = t0 - t1;
+        }
+      }
+      if (PF) load_tile(tile + tstride, nxt);
+#pragma unroll
+      for (int hh = 2; hh < HALF; hh <<= 1) {
+#pragma unroll
+        for (int i = 0; i < HALF; ++i) {
+          if ((i & hh) == 0) {
+            const float a = x[i], b = x[i + hh];
+            x[i] = a + b;
+            x[i + hh] = a - b;
+          }
         }
       }
     }
@@ -600,15 +668,15 @@ __global__ __launch_bounds__(HalfLaunch<PROD>::kWaves * kWave, HalfLaunch<PROD>:
       float r = 0.f;
       if constexpr (USE_LUT) {
         const float uu = fmaf(x[i], ua, lut_b);
-        const float2 e = s_lut[(uint32_t)uu];
+        const float2 e = T.lut[(uint32_t)uu];
         c = __float_as_int(e.y) + (uu >= e.x ? 1 : 0);
-        if constexpr (PROD) r = fmaf(x[i], inv_p, -s_cent[c]);
+        if constexpr (PROD) r = fmaf(x[i], inv_p, -T.cent[c]);
       } else {
         const float z = x[i] * inv_p;
         c = 0;
 #pragma unroll
         for (int k = 0; k < NTH; ++k) c += (z >= p.codec.thresholds[k] * cscale) ? 1 : 0;
-        if constexpr (PROD) r = z - s_cent[c];
+        if constexpr (PROD) r = z - T.cent[c];
       }
       const int off = i * CB;
       words[off >> 5] |= (uint32_t)c << (off & 31);
@@ -661,10 +729,10 @@ __global__ __launch_bounds__(HalfLaunch<PROD>::kWaves * kWave, HalfLaunch<PROD>:
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           const int f0 = (2 * mp) * KS + ks, f1 = (2 * mp + 1) * KS + ks;
-          const half8_t a0h = __builtin_bit_cast(half8_t, s_frag[(2 * f0) * kWave + lane]);
-          const half8_t a0l = __builtin_bit_cast(half8_t, s_frag[(2 * f0 + 1) * kWave + lane]);
-          const half8_t a1h = __builtin_bit_cast(half8_t, s_frag[(2 * f1) * kWave + lane]);
-          const half8_t a1l = __builtin_bit_cast(half8_t, s_frag[(2 * f1 + 1) * kWave + lane]);
+          const half8_t a0h = __builtin_bit_cast(half8_t, T.frag[(2 * f0) * kWave + lane]);
+          const half8_t a0l = __builtin_bit_cast(half8_t, T.frag[(2 * f0 + 1) * kWave + lane]);
+          const half8_t a1h = __builtin_bit_cast(half8_t, T.frag[(2 * f1) * kWave + lane]);
+          const half8_t a1l = __builtin_bit_cast(half8_t, T.frag[(2 * f1 + 1) * kWave + lane]);
           const half8_t rh = __builtin_bit_cast(half8_t, make_uint4(bh[ks][0], bh[ks][1], bh[ks][2], bh[ks][3]));
           const half8_t rl = __builtin_bit_cast(half8_t, make_uint4(bl[ks][0], bl[ks][1], bl[ks][2], bl[ks][3]));
           c0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0h, rh, c0, 0, 0, 0);
@@ -707,6 +775,62 @@ __global__ __launch_bounds__(HalfLaunch<PROD>::kWaves * kWave, HalfLaunch<PROD>:
       }
     }
   }
+}
+
+template <int D, int CB, bool PROD>
+__global__ __launch_bounds__(HalfLaunch<PROD>::kWaves * kWave, HalfLaunch<PROD>::kMinWavesPerEU) void encode_half_kernel(EncodeParams p) {
+  constexpr int kHalfWaves = HalfLaunch<PROD>::kWaves;
+  constexpr bool PF = HalfLaunch<PROD>::kPrefetch;
+  __shared__ HalfTables<D, CB, PROD> T;
+  const int tid = threadIdx.x;
+  const EncodeParams* kp = (const EncodeParams*)__builtin_amdgcn_kernarg_segment_ptr();
+  const int64_t tstride = (int64_t)gridDim.x * kHalfWaves;
+  const int64_t tile = (int64_t)blockIdx.x * kHalfWaves + (tid >> 6);
+  uint32_t nxt[D / 4];
+  // the first tile's input is in flight during the set-up
+  if (PF) half_load<D>(p, tile, nxt);
+  half_setup<D, CB, PROD>(p, kp, T, tid, blockDim.x);
+  __syncthreads();
+  half_tiles<D, CB, PROD, PF>(p, T, tile, tstride, nxt);
+}
+
+// Keys (prod) and values (mse) of one call in one launch.  Each SIMD runs
+// two key waves and one value wave: the value waves' loads and stores
+// overlap the key waves' arithmetic.  Waves 0..7 of a workgroup encode key
+// tiles, waves 8..11 value tiles (measured against 6 + 6, 4 + 8 and 9 + 3).
+// Only the value waves load their next tile ahead: the key waves'
+// registers leave no room for it at three waves per SIMD.
+struct EncodeKVParams {
+  EncodeParams k, v;
+};
+constexpr int kKVKeyWaves = 8, kKVValWaves = 4;
+static_assert(sizeof(EncodeKVParams) <= 4096, "kernel argument segment");
+
+// The value waves rotate on the matrix cores (H D as a +-1 matrix times
+// the fp16 input): it moves their butterflies off the vector ALU, which the
+// key waves keep busy.  The key waves keep the butterflies (their matrix
+// cores already run the S r products).
+constexpr bool kKVRotK = false, kKVRotV = true;
+
+template <int D, int CBK, int CBV>
+__global__ __launch_bounds__((kKVKeyWaves + kKVValWaves) * kWave, 3) void encode_kv_half_kernel(EncodeKVParams pp) {
+  __shared__ HalfTables<D, CBK, true, kKVRotK> TK;
+  __shared__ HalfTables<D, CBV, false, kKVRotV> TV;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const EncodeKVParams* kpp = (const EncodeKVParams*)__builtin_amdgcn_kernarg_segment_ptr();
+  const bool key_wave = wave < kKVKeyWaves;
+  const int64_t vtile = (int64_t)blockIdx.x * kKVValWaves + (wave - kKVKeyWaves);
+  uint32_t nxt[D / 4];
+  // a value wave's first tile is in flight during the set-up
+  if (!key_wave) half_load<D>(pp.v, vtile, nxt);
+  half_setup<D, CBK, true, kKVRotK>(pp.k, &kpp->k, TK, tid, blockDim.x);
+  half_setup<D, CBV, false, kKVRotV>(pp.v, &kpp->v, TV, tid, blockDim.x);
+  __syncthreads();
+  if (key_wave)
+    half_tiles<D, CBK, true, false, kKVRotK>(pp.k, TK, (int64_t)blockIdx.x * kKVKeyWaves + wave,
+                                             (int64_t)gridDim.x * kKVKeyWaves, nxt);
+  else
+    half_tiles<D, CBV, false, true, kKVRotV>(pp.v, TV, vtile, (int64_t)gridDim.x * kKVValWaves, nxt);
 }
 
 template <int D, int CB, bool PROD>
@@ -808,12 +932,10 @@ static bool build_grid(const tq_codec& c, EncodeParams& p) {
   return false;
 }
 
-hipError_t launch_encode(const tq_codec& c, const void* x, int dtype, int64_t n_rows,
-                         const RopeHost& rope, const tq_packed& out, void* workspace,
-                         hipStream_t stream) {
-  if (n_rows == 0) return hipSuccess;
-  if (c.d == 1536) return launch_wide_encode(c, x, dtype, n_rows, out, workspace, stream);
-  EncodeParams p = {};
+// Kernel arguments for one codec (false: no quantizer grid fits).
+static bool fill_params(const tq_codec& c, const void* x, int64_t n_rows, const RopeHost& rope,
+                        const tq_packed& out, EncodeParams& p) {
+  p = {};
   p.x = x;
   p.n_rows = n_rows;
   p.idx = out.idx;
@@ -840,10 +962,80 @@ hipError_t launch_encode(const tq_codec& c, const void* x, int dtype, int64_t n_
     for (int i = 0; i < c.d / 2 && i < 64; ++i)
       p.theta[i] = std::pow((double)rope.base, -2.0 * i / (double)c.d);
   }
-  if (c.code_bits >= 3 && !build_grid(c, p)) return hipErrorInvalidValue;
+  return c.code_bits < 3 || build_grid(c, p);
+}
+
+hipError_t launch_encode(const tq_codec& c, const void* x, int dtype, int64_t n_rows,
+                         const RopeHost& rope, const tq_packed& out, void* workspace,
+                         hipStream_t stream) {
+  if (n_rows == 0) return hipSuccess;
+  if (c.d == 1536) return launch_wide_encode(c, x, dtype, n_rows, out, workspace, stream);
+  EncodeParams p;
+  if (!fill_params(c, x, n_rows, rope, out, p)) return hipErrorInvalidValue;
   if (c.d == 128) return pick_rest<128>(c, dtype, rope.on, p, stream);
   if (c.d == 64) return pick_rest<64>(c, dtype, rope.on, p, stream);
   return hipErrorInvalidValue;
+}
+
+template <int D, int CBK, int CBV>
+static hipError_t run_kv_half(const EncodeKVParams& pp, hipStream_t stream) {
+  static int per_cu = 0;
+  constexpr int kThreads = (kKVKeyWaves + kKVValWaves) * kWave;
+  if (per_cu == 0) {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, encode_kv_half_kernel<D, CBK, CBV>, kThreads, 0) !=
+            hipSuccess || nb < 1)
+      nb = 1;
+    per_cu = nb;
+  }
+  // enough workgroups for every key wave to have a tile, at most what fits
+  const int64_t ntiles = (pp.k.n_rows + 31) / 32;
+  int64_t blocks = (ntiles + kKVKeyWaves - 1) / kKVKeyWaves;
+  const int64_t cap = (int64_t)device_cu_count() * per_cu;
+  if (blocks > cap) blocks = cap;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL((encode_kv_half_kernel<D, CBK, CBV>), dim3((unsigned)blocks), dim3(kThreads), 0,
+                     stream, pp);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t pick_kv(int cbk, int cbv, const EncodeKVParams& pp, hipStream_t s) {
+  if constexpr (D == 64) {
+    switch (cbk * 8 + cbv) {
+      case 1 * 8 + 2: return run_kv_half<D, 1, 2>(pp, s);
+      case 1 * 8 + 3: return run_kv_half<D, 1, 3>(pp, s);
+      case 1 * 8 + 4: return run_kv_half<D, 1, 4>(pp, s);
+    }
+  }
+  switch (cbk * 8 + cbv) {
+    case 2 * 8 + 2: return run_kv_half<D, 2, 2>(pp, s);
+    case 2 * 8 + 3: return run_kv_half<D, 2, 3>(pp, s);
+    case 2 * 8 + 4: return run_kv_half<D, 2, 4>(pp, s);
+    case 3 * 8 + 2: return run_kv_half<D, 3, 2>(pp, s);
+    case 3 * 8 + 3: return run_kv_half<D, 3, 3>(pp, s);
+    case 3 * 8 + 4: return run_kv_half<D, 3, 4>(pp, s);
+  }
+  return hipErrorNotSupported;
+}
+
+bool encode_kv_fusable(const tq_codec& kc, const tq_codec& vc, int dtype, bool rope) {
+  if (dtype != TQ_F16 || rope || kc.d != vc.d || (kc.d != 64 && kc.d != 128)) return false;
+  if (kc.mode != TQ_PROD || vc.mode != TQ_MSE) return false;
+  // (1-bit key tables at d = 128 would spill at three waves per SIMD)
+  const int kmin = kc.d == 128 ? 2 : 1;
+  return kc.code_bits >= kmin && kc.code_bits <= 3 && vc.code_bits >= 2 && vc.code_bits <= 4;
+}
+
+hipError_t launch_encode_kv(const tq_codec& kc, const tq_codec& vc, const void* k, const void* v,
+                            int64_t n_rows, const tq_packed& kout, const tq_packed& vout,
+                            hipStream_t stream) {
+  if (n_rows == 0) return hipSuccess;
+  EncodeKVParams pp;
+  if (!fill_params(kc, k, n_rows, RopeHost{}, kout, pp.k) || !fill_params(vc, v, n_rows, RopeHost{}, vout, pp.v))
+    return hipErrorInvalidValue;
+  if (kc.d == 128) return pick_kv<128>(kc.code_bits, vc.code_bits, pp, stream);
+  return pick_kv<64>(kc.code_bits, vc.code_bits, pp, stream);
 }
 
 }  // namespace tqk

@@ -21,6 +21,14 @@ hipError_t launch_encode(const tq_codec& c, const void* x, int dtype,
                          int64_t n_rows, const RopeHost& rope,
                          const tq_packed& out, void* workspace, hipStream_t stream);
 
+// Keys (prod) and values (mse) of one call in a single launch, for fp16
+// inputs without RoPE at d = 64 or 128 and the code widths encode_kv_fusable
+// accepts; the results equal two launch_encode calls.
+bool encode_kv_fusable(const tq_codec& kc, const tq_codec& vc, int dtype, bool rope);
+hipError_t launch_encode_kv(const tq_codec& kc, const tq_codec& vc, const void* k, const void* v,
+                            int64_t n_rows, const tq_packed& kout, const tq_packed& vout,
+                            hipStream_t stream);
+
 // d = 1536 (wide.hip).  The encode workspace holds S as fp16 hi / lo planes
 // and the residual planes of one block of vectors (prod only); the scan
 // workspace holds the S planes and the four query planes.

@@ -187,3 +187,33 @@ def test_encode_llama_slice():
     check_prod(to_np(k).astype(np.float64).reshape(-1, 128), kout, kc, p["codec"], rk)
     check_mse(to_np(v).astype(np.float64).reshape(-1, 128), vout, vc, p["codec"], rv)
     print("K", rk, "V", rv)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("kbits,vbits", [(2, 2), (2, 4), (3, 3), (4, 2), (4, 3), (4, 4)])
+def test_encode_kv_one_launch_equals_two(d, kbits, vbits):
+    """fp16 keys (prod) and values (mse) given together run as one launch
+    (except 1-bit key tables at d = 128, which take two); every output byte
+    must equal the key-only and value-only calls, over a ragged count (tiles
+    of 32 rows, the last one partial) with a zero row."""
+    say("encode one launch vs two d=%d K prod b=%d V mse b=%d" % (d, kbits, vbits))
+    rng = np.random.default_rng(7000 + 100 * d + 10 * kbits + vbits)
+    n = 32 * 77 + 13
+    k = (rng.standard_normal((n, d)) * rng.uniform(0.1, 10, (n, 1))).astype(np.float16)
+    v = (rng.standard_normal((n, d)) * rng.uniform(0.1, 10, (n, 1))).astype(np.float16)
+    k[9] = 0.0
+    v[10] = 0.0
+    draws = synth.codec_draws(rng, d, m=d)
+    vdraws = synth.codec_draws(rng, d, m=0)
+    kc = make_codec(d, tq.TQ_PROD, kbits, draws)
+    vc = make_codec(d, tq.TQ_MSE, vbits, vdraws)
+    kt, vt = torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda()
+    ka, va = tq.encode_kv(kc, vc, kt, vt)
+    kb, _ = tq.encode_kv(kc, None, kt, None)
+    _, vb = tq.encode_kv(None, vc, None, vt)
+    torch.cuda.synchronize()
+    for x, y in ((ka.idx, kb.idx), (ka.qjl, kb.qjl), (ka.norm, kb.norm), (ka.rnorm, kb.rnorm),
+                 (va.idx, vb.idx), (va.norm, vb.norm)):
+        assert torch.equal(x, y)
+    check_prod(k.astype(np.float64), ka, kc, draws)
+    check_mse(v.astype(np.float64), va, vc, vdraws)
