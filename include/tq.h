@@ -156,6 +156,23 @@ int tq_encode_kv(const tq_codec* kc, const tq_codec* vc, const void* k,
                  const tq_packed* kout, const tq_packed* vout, void* workspace,
                  size_t workspace_bytes, tq_stream_t stream);
 
+/* ---- decode: packed rows back to vectors ---------------------------------
+ * The materializing decoder ("FibQuant", "2.3 Codifica e Decodifica": look
+ * the centroids up, rotate back, rescale by the norm; "Google presenta
+ * TurboQuant", unbiased prod section for the QJL term):
+ *   TQ_MSE:  x_hat = nu * Pi^T c[idx]
+ *   TQ_PROD: x_hat = nu * Pi^T (c[idx] + sqrt(pi/2)/m * gamma * S^T (2 sigma - 1))
+ * with Pi^T w = D (H_d w) / sqrt(d).  It is the first pass of a two-pass
+ * attention (decode, then plain attention on the vectors); tq_attend_decode
+ * does not need it.
+ *   c     host codec, d = 64 or 128 (other d: TQ_ERR_UNSUPPORTED)
+ *   in    host struct of device planes holding n_rows rows
+ *   out   device [n_rows][d] of out_dtype (TQ_F16, rounded toward zero, or
+ *         TQ_F32), 16-byte aligned; written only
+ * Returns TQ_OK, TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED or TQ_ERR_HIP. */
+int tq_decode_kv(const tq_codec* c, const tq_packed* in, int64_t n_rows, void* out,
+                 int out_dtype, tq_stream_t stream);
+
 /* ---- a8..a11: attention from codes ----------------------------------------
  * For every batch b, query head h (KV head g = h / (hq / hkv)) and query a:
  *   s_j = scale * nu_j * ( <q', c_K[idx_j]> + sqrt(pi/2)/m * gamma_j *

@@ -23,7 +23,7 @@ TQ_MSE, TQ_PROD = 0, 1
 TQ_F16, TQ_F32 = 0, 1
 
 EXPORTS = ("tq_status_string", "tq_build_codebook", "tq_codec_init", "tq_encode_kv_workspace",
-           "tq_encode_kv",
+           "tq_encode_kv", "tq_decode_kv",
            "tq_attend_decode_workspace", "tq_attend_decode",
            "tq_inner_product_workspace", "tq_inner_product")
 
@@ -75,6 +75,8 @@ def lib():
     L.tq_encode_kv.argtypes = [ctypes.POINTER(TQCodec), ctypes.POINTER(TQCodec), P, P, I, I64,
                                ctypes.POINTER(TQRope), ctypes.POINTER(TQPacked),
                                ctypes.POINTER(TQPacked), P, SZ, P]
+    L.tq_decode_kv.restype = I
+    L.tq_decode_kv.argtypes = [ctypes.POINTER(TQCodec), ctypes.POINTER(TQPacked), I64, P, I, P]
     L.tq_attend_decode_workspace.restype = SZ
     L.tq_attend_decode_workspace.argtypes = [I, I, I, I, I64, I]
     L.tq_attend_decode.restype = I
@@ -241,6 +243,21 @@ def encode_kv(kcodec, vcodec, k, v, rope=None, kout=None, vout=None, workspace=N
                             wbytes, _stream(stream))
     _check(st, "tq_encode_kv")
     return kout, vout
+
+
+def decode_kv(codec, pk, n, dtype=None, out=None, stream=None):
+    """Packed rows back to vectors: returns out [n, d] (float16 unless dtype
+    or out says float32)."""
+    if out is None:
+        dt = dtype if dtype is not None else torch.float16
+        out = torch.empty((n, codec.d), dtype=dt, device=pk.idx.device)
+    _device_tensor(out, "out")
+    if out.numel() != n * codec.d:
+        raise ValueError("out must hold n x d elements")
+    st = lib().tq_decode_kv(ctypes.byref(codec.struct), ctypes.byref(pk.struct), int(n), _ptr(out),
+                            _dtype_code(out), _stream(stream))
+    _check(st, "tq_decode_kv")
+    return out
 
 
 def attend_workspace_bytes(batch, n_q, hq, hkv, ctx, d):

@@ -119,6 +119,19 @@ extern "C" int tq_encode_kv(const tq_codec* kc, const tq_codec* vc, const void* 
   return TQ_OK;
 }
 
+extern "C" int tq_decode_kv(const tq_codec* c, const tq_packed* in, int64_t n_rows, void* out,
+                            int out_dtype, tq_stream_t stream) {
+  int st = check_codec(c);
+  if (st != TQ_OK) return st;
+  if (c->d != 64 && c->d != 128) return TQ_ERR_UNSUPPORTED;
+  if ((st = check_planes(c, in)) != TQ_OK) return st;
+  if (n_rows < 0 || (out_dtype != TQ_F16 && out_dtype != TQ_F32)) return TQ_ERR_INVALID_ARG;
+  if (n_rows == 0) return TQ_OK;
+  if (out == nullptr || !aligned(out, 16)) return TQ_ERR_INVALID_ARG;
+  return hip_status(tqk::launch_materialize(*c, *in, n_rows, out, out_dtype,
+                                            reinterpret_cast<hipStream_t>(stream)));
+}
+
 extern "C" size_t tq_attend_decode_workspace(int batch, int n_q, int hq, int hkv,
                                              int64_t ctx, int d) {
   if (batch <= 0 || n_q <= 0 || hq <= 0 || hkv <= 0 || ctx <= 0 || d <= 0) return 0;

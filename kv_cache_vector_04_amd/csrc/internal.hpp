@@ -29,6 +29,10 @@ hipError_t launch_encode_kv(const tq_codec& kc, const tq_codec& vc, const void* 
                             int64_t n_rows, const tq_packed& kout, const tq_packed& vout,
                             hipStream_t stream);
 
+// Packed rows back to vectors (materialize.hip): n_rows x d of out_dtype.
+hipError_t launch_materialize(const tq_codec& c, const tq_packed& in, int64_t n_rows, void* out,
+                              int out_dtype, hipStream_t stream);
+
 // d = 1536 (wide.hip).  The encode workspace holds S as fp16 hi / lo planes
 // and the residual planes of one block of vectors (prod only); the scan
 // workspace holds the S planes and the four query planes.

@@ -107,6 +107,28 @@ def test_encode_validation_before_launch(L):
     assert L.tq_encode_kv_workspace(None, ctypes.byref(_codec_struct(L, 1536, tq.TQ_MSE, 2)), 1 << 20) == 0
 
 
+def test_decode_validation_before_launch(L):
+    kc = _codec_struct(L, 128, tq.TQ_PROD, 4)
+    vc = _codec_struct(L, 64, tq.TQ_MSE, 3)
+    fake = ctypes.c_void_p(1 << 20)
+    pk = tq.TQPacked(1 << 20, 1 << 20, 1 << 20, 1 << 20)
+    pv = tq.TQPacked(1 << 20, None, 1 << 20, None)
+    dec = L.tq_decode_kv
+    assert dec(None, ctypes.byref(pk), 10, fake, tq.TQ_F16, None) == tq.TQ_ERR_INVALID_ARG
+    # prod rows need their QJL planes
+    assert dec(ctypes.byref(kc), ctypes.byref(pv), 10, fake, tq.TQ_F16, None) == tq.TQ_ERR_INVALID_ARG
+    assert dec(ctypes.byref(kc), ctypes.byref(pk), -1, fake, tq.TQ_F16, None) == tq.TQ_ERR_INVALID_ARG
+    assert dec(ctypes.byref(kc), ctypes.byref(pk), 10, fake, 7, None) == tq.TQ_ERR_INVALID_ARG
+    assert dec(ctypes.byref(vc), ctypes.byref(pv), 10, None, tq.TQ_F32, None) == tq.TQ_ERR_INVALID_ARG
+    assert dec(ctypes.byref(vc), ctypes.byref(pv), 10, ctypes.c_void_p((1 << 20) + 4), tq.TQ_F32,
+               None) == tq.TQ_ERR_INVALID_ARG
+    # n_rows = 0 launches nothing
+    assert dec(ctypes.byref(vc), ctypes.byref(pv), 0, None, tq.TQ_F32, None) == tq.TQ_OK
+    # the decoder covers d = 64 and 128
+    wide = _codec_struct(L, 1536, tq.TQ_MSE, 2)
+    assert dec(ctypes.byref(wide), ctypes.byref(pv), 10, fake, tq.TQ_F16, None) == tq.TQ_ERR_UNSUPPORTED
+
+
 def test_wide_encode_workspace(L):
     kw = _codec_struct(L, 1536, tq.TQ_PROD, 2)
     fake = ctypes.c_void_p(1 << 20)
