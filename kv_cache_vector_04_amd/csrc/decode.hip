@@ -181,11 +181,8 @@ __global__ __launch_bounds__(DecWaves<CBV>::kThreads) void decode_kernel(DecodeP
   __shared__ __align__(16) unsigned char s_wn[Gm::WN_B];     // weights (nibble sums in set-up)
   __shared__ __align__(16) float4 s_qT[D];                    // q_rot, 4 rows per coordinate
   __shared__ __align__(16) float4 s_sT[D];                    // Sq, 4 rows per coordinate
-  __shared__ float s_qr[kDecRows][D];
   __shared__ float s_tot[kDecRows];
   __shared__ float s_kc[16], s_vc[16];
-  __shared__ uint32_t s_kflip[D / 32];
-  __shared__ double s_theta[D / 2];
   // 3-bit value codes: the lane groups' 24 bits straddle words, so each
   // wave stages its tile's value rows here instead of holding two words per
   // token in registers
@@ -252,68 +249,74 @@ __global__ __launch_bounds__(DecWaves<CBV>::kThreads) void decode_kernel(DecodeP
     s_kc[tid] = kp->kcent[tid];
     s_vc[tid] = kp->vcent[tid];
   }
-  if (tid >= 64 && tid < 64 + D / 32) s_kflip[tid - 64] = kp->kflip[tid - 64];
-  if (tid >= 128 && tid < 128 + D / 2) s_theta[tid - 128] = kp->theta[tid - 128];
-  constexpr int PER = (kDecRows * D + kDecThreads - 1) / kDecThreads;
-  for (int t = tid; t < kDecRows * D; t += kDecThreads) {
-    const int r = t / D, i = t % D;
-    float v = 0.f;
-    if (r < nrows) {
-      const int64_t off = (row_base + r) * D + i;
-      v = p.q_f16 ? (float)reinterpret_cast<const _Float16*>(p.q)[off]
-                  : reinterpret_cast<const float*>(p.q)[off];
-    }
-    s_qr[r][i] = v;
-  }
-  __syncthreads();
-  // q' = RoPE(q), sign flip, natural-order butterflies through LDS
-  float qv[PER];
+  // q' = RoPE(q), sign flip and the natural-order butterflies: wave r < 4
+  // rotates query row r in registers, lane l holding coordinates C l + c
+  // (C = d / 64): the stages on coordinate bits below log2 C stay in the
+  // lane, the others exchange with lane l ^ 2^(bit - log2 C)
+  constexpr int C = D / kWave;
+  if (wave < kDecRows) {
+    const int r = wave;
+    float x[C];
 #pragma unroll
-  for (int u = 0; u < PER; ++u) {
-    const int t = tid + u * kDecThreads;
-    qv[u] = 0.f;
-    if (t < kDecRows * D) {
-      const int r = t / D, i = t % D;
-      float x = s_qr[r][i];
-      if (p.rope) {
-        const int pr = i >> 1;
-        const int64_t pos = (int64_t)p.pos0 + ((lr0 + r) % p.n_q);
+    for (int c = 0; c < C; ++c) {
+      const int i = C * lane + c;
+      float v = 0.f;
+      if (r < nrows) {
+        const int64_t off = (row_base + r) * D + i;
+        v = p.q_f16 ? (float)reinterpret_cast<const _Float16*>(p.q)[off]
+                    : reinterpret_cast<const float*>(p.q)[off];
+      }
+      x[c] = v;
+    }
+    if (p.rope) {
+      // interleaved pairs (2 pr, 2 pr + 1) rotated by pos * theta_pr
+      const int64_t pos = (int64_t)p.pos0 + ((lr0 + r) % p.n_q);
+      if constexpr (C == 2) {
         float sn, cs;
-        sincos_reduced((double)pos * s_theta[pr], sn, cs);
-        const float a = s_qr[r][2 * pr], bb = s_qr[r][2 * pr + 1];
-        x = (i & 1) ? (a * sn + bb * cs) : (a * cs - bb * sn);
-      }
-      const uint32_t bit = (s_kflip[i >> 5] >> (i & 31)) & 1u;
-      qv[u] = bit ? -x : x;
-    }
-  }
-  for (int h = 1; h < D; h <<= 1) {
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int t = tid + u * kDecThreads;
-      if (t < kDecRows * D) s_qr[t / D][t % D] = qv[u];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int t = tid + u * kDecThreads;
-      if (t < kDecRows * D) {
-        const int r = t / D, i = t % D;
-        const float o = s_qr[r][i ^ h];
-        qv[u] = (i & h) ? (o - qv[u]) : (qv[u] + o);
+        sincos_reduced((double)pos * kp->theta[lane], sn, cs);
+        const float a = x[0], bb = x[1];
+        x[0] = a * cs - bb * sn;
+        x[1] = a * sn + bb * cs;
+      } else {
+        const int i = lane;
+        float sn, cs;
+        sincos_reduced((double)pos * kp->theta[i >> 1], sn, cs);
+        const float o = __shfl_xor(x[0], 1);
+        const float a = (i & 1) ? o : x[0], bb = (i & 1) ? x[0] : o;
+        x[0] = (i & 1) ? (a * sn + bb * cs) : (a * cs - bb * sn);
       }
     }
-  }
-  // q_rot, 4 rows per coordinate
 #pragma unroll
-  for (int u = 0; u < PER; ++u) {
-    const int t = tid + u * kDecThreads;
-    if (t < kDecRows * D)
-      reinterpret_cast<float*>(s_qT)[4 * (t % D) + t / D] = qv[u] * p.inv_sqrt_d;
+    for (int c = 0; c < C; ++c) {
+      const int i = C * lane + c;
+      if ((kp->kflip[i >> 5] >> (i & 31)) & 1u) x[c] = -x[c];
+    }
+#pragma unroll
+    for (int hb = 1; hb < C; hb <<= 1)
+#pragma unroll
+      for (int c = 0; c < C; ++c)
+        if ((c & hb) == 0) {
+          const float a = x[c], bb = x[c + hb];
+          x[c] = a + bb;
+          x[c + hb] = a - bb;
+        }
+#pragma unroll
+    for (int lb = 1; lb < kWave; lb <<= 1) {
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        const float o = __shfl_xor(x[c], lb);
+        x[c] = (lane & lb) ? (o - x[c]) : (x[c] + o);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+      reinterpret_cast<float*>(s_qT)[4 * (C * lane + c) + r] = x[c] * p.inv_sqrt_d;
   }
-  __syncthreads();
-  // Sq partial sums over this thread's k-part, then a reduction over parts
+  __syncthreads();                                  // q_rot and the centroids in LDS
+  // Sq partial sums over this thread's k-part (into the weight buffer, free
+  // until the scan); the other threads build the key and value tables
+  float4* s_sqp = reinterpret_cast<float4*>(s_wn);
+  static_assert(KP * D * 16 <= Gm::WN_B, "Sq partials fit the weight buffer");
   if (sq_thread) {
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
@@ -324,16 +327,30 @@ __global__ __launch_bounds__(DecWaves<CBV>::kThreads) void decode_kernel(DecodeP
       a = f4fma(s_qT[k + 2], srow[j].z, a);
       a = f4fma(s_qT[k + 3], srow[j].w, a);
     }
-    reinterpret_cast<float4*>(s_tab)[spart * D + si] = a;
+    s_sqp[spart * D + si] = a;
   }
-  __syncthreads();
-  if (tid < D) {
-    float4 a = reinterpret_cast<const float4*>(s_tab)[tid];
+  {
+    // LK: lanes over table values, all threads (the Sq threads join after
+    // their partial sums)
+    for (int t = tid; t < NF * NE; t += kDecThreads) {
+      const int v = t % NE, f = t / NE;
+      float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int q = 1; q < KP; ++q) a = f4add(a, reinterpret_cast<const float4*>(s_tab)[q * D + tid]);
+      for (int e = 0; e < KG::gk; ++e)
+        a = f4fma(s_qT[f * KG::gk + e], s_kc[(v >> (e * CBK)) & ((1 << CBK) - 1)], a);
+      s_lk[t] = a;
+    }
+  }
+  for (int t = tid; t < NVE; t += kDecThreads)
+    s_lv[t] = make_float2(s_vc[t & ((1 << CBV) - 1)], s_vc[t >> CBV]);
+  __syncthreads();                                  // Sq partials, LK, LV
+  if (tid < D) {
+    float4 a = s_sqp[tid];
+#pragma unroll
+    for (int q = 1; q < KP; ++q) a = f4add(a, s_sqp[q * D + tid]);
     s_sT[tid] = a;
   }
-  __syncthreads();
+  __syncthreads();                                  // Sq
   // tot[r] = sum_i Sq[r][i]: one wave per row
   if (wave < kDecRows) {
     float t = 0.f;
@@ -350,20 +367,7 @@ __global__ __launch_bounds__(DecWaves<CBV>::kThreads) void decode_kernel(DecodeP
       if ((n >> e) & 1) a = f4add(a, s_sT[8 * pb + 4 * h + e]);
     s_nib[t] = a;
   }
-  // LK: lanes over table values (this thread's centroids stay in registers)
-  {
-    for (int t = tid; t < NF * NE; t += kDecThreads) {
-      const int v = t % NE, f = t / NE;
-      float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-      for (int e = 0; e < KG::gk; ++e)
-        a = f4fma(s_qT[f * KG::gk + e], s_kc[(v >> (e * CBK)) & ((1 << CBK) - 1)], a);
-      s_lk[t] = a;
-    }
-  }
-  for (int t = tid; t < NVE; t += kDecThreads)
-    s_lv[t] = make_float2(s_vc[t & ((1 << CBV) - 1)], s_vc[t >> CBV]);
-  __syncthreads();
+  __syncthreads();                                  // nibble sums, tot
   for (int t = tid; t < NB * 256; t += kDecThreads) {
     const int pb = t >> 8, v = t & 255;
     s_lq[t] = f4add(s_nib[pb * 32 + (v & 15)], s_nib[pb * 32 + 16 + (v >> 4)]);
