@@ -38,6 +38,9 @@ from .codec import (encode_mse, encode_prod, decode_mse, decode_prod,
 from .rope import rope_interleaved
 from .attention import attention_from_codes, attention_materialized
 from .search import inner_product_matrix, top_k
+from .fibquant import (block_pdf, spiral_init, quadrature, nearest, block_mse,
+                       lloyd, fibquant_codebook, encode_vq, decode_vq, pack_vq,
+                       unpack_vq)
 
 __all__ = [
     "beta_coord_pdf", "lloyd_max", "codebook", "distortion", "cell_moments",
@@ -46,5 +49,7 @@ __all__ = [
     "decode_mse", "decode_prod", "estimate_ip", "pack_codes", "unpack_codes",
     "pack_bits", "unpack_bits", "EncodedMSE", "EncodedProd", "qjl_factor",
     "qjl_projection", "rope_interleaved", "attention_from_codes",
-    "attention_materialized", "inner_product_matrix", "top_k",
+    "attention_materialized", "inner_product_matrix", "top_k", "block_pdf",
+    "spiral_init", "quadrature", "nearest", "block_mse", "lloyd",
+    "fibquant_codebook", "encode_vq", "decode_vq", "pack_vq", "unpack_vq",
 ]
