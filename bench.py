@@ -51,12 +51,14 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sets", type=int, default=8)
     ap.add_argument("--workload", default="gqa_decode",
-                    choices=("gqa_decode", "llama_prefill", "esm2", "vector_search"),
+                    choices=("gqa_decode", "llama_prefill", "esm2", "vector_search", "fibquant"),
                     help="gqa_decode (the default bench line); llama_prefill (32 layers x 8 KV "
                          "heads x 131072 tokens, 3-bit, encode + one decode step per layer); "
                          "esm2 (33 layers x 64 x 20 heads x 1024 tokens, d64, RoPE keys, 3-bit, "
                          "encode + bidirectional attention); vector_search (1e6 x d1536 encode "
-                         "+ 1024-query scan with top-10)")
+                         "+ 1024-query scan with top-10); fibquant (the GQA K/V, 2 x 262144 "
+                         "rows d128, through the k = 2 vector code at N = 32, 2.5 bits, "
+                         "encode + decode, with a sweep over N)")
     a = ap.parse_args()
     heavy = a.workload != "gqa_decode"
     if a.steps is None:
@@ -81,6 +83,8 @@ def main():
     torch.cuda.set_device(dev)
     if a.workload == "vector_search":
         return bench_search(a, torch, synth, tq, dev)
+    if a.workload == "fibquant":
+        return bench_fibquant(a, torch, synth, tq, dev)
     if a.workload in ("llama_prefill", "esm2"):
         return bench_layers(a, torch, synth, tq, dev)
     hkv, ctx, d, hq = 8, 32768, 128, 32
@@ -435,6 +439,123 @@ def bench_search(a, torch, synth, tq, dev):
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_search(p, data)
     print(json.dumps(res), flush=True)
+
+
+FP32_VECTOR_PEAK_TFLOPS = 157.3
+
+
+def bench_fibquant(a, torch, synth, tq, dev, n_main=32, sweep=(4, 16, 32, 64, 256)):
+    """FibQuant k = 2 over the GQA decode workload's K and V (8 KV heads x
+    32768 tokens x 128, fp16): a step encodes both to block codes at
+    N = 32 (2.5 bits per coordinate) and decodes both back to fp16.  Each N
+    of the sweep is timed with HIP events on the launch stream (median over
+    the steps).  The encoder's nearest search tests every codeword: 4 flops
+    (two FMAs) per (block, codeword), ALU-bound; the decoder moves
+    2 d + d/2 log2(N)/8 + 4 bytes per row."""
+    w = synth.gqa_decode()
+    d = 128
+    k = torch.from_numpy(w["k"].reshape(-1, d)).to(dev)
+    v = torch.from_numpy(w["v"].reshape(-1, d)).to(dev)
+    n = k.shape[0]
+    flip = w["codec"].flip
+
+    def setup(nc):
+        c = tq.VQCodec(d, nc, flip)
+        bufs = [(torch.empty((n, c.row_bytes), dtype=torch.uint8, device=dev),
+                 torch.empty((n,), dtype=torch.float32, device=dev),
+                 torch.empty((n, d), dtype=torch.float16, device=dev)) for _ in range(2)]
+        return c, bufs
+
+    def parts(c, bufs):
+        def enc():
+            for x, (i, nu, _) in zip((k, v), bufs):
+                tq.encode_vq(c, x, idx=i, norm=nu)
+
+        def dec():
+            for i, nu, o in bufs:
+                tq.decode_vq(c, i, nu, n, out=o)
+        return enc, dec
+
+    def timed(fns, steps):
+        for _ in range(max(1, a.warmup)):
+            for f in fns:
+                f()
+        torch.cuda.synchronize()
+        ts = [[] for _ in fns]
+        for _ in range(steps):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
+            ev[0].record()
+            for j, f in enumerate(fns):
+                f()
+                ev[j + 1].record()
+            torch.cuda.synchronize()
+            for j in range(len(fns)):
+                ts[j].append(ev[j].elapsed_time(ev[j + 1]) * 1e-3)
+        return [float(np.median(t)) for t in ts]
+
+    rows_sweep = []
+    for nc in sweep:
+        c, bufs = setup(nc)
+        te, td = timed(parts(c, bufs), max(5, min(a.steps, 20)))
+        bb = int(round(np.log2(nc)))
+        rows_sweep.append({"N": nc, "bits_per_coord": bb / 2.0, "encode_us": te * 1e6,
+                           "encode_vectors_per_s": 2 * n / te,
+                           "encode_TFLOP_per_s": 4.0 * nc * (d // 2) * 2 * n / te / 1e12,
+                           "decode_us": td * 1e6,
+                           "decode_GB_per_s": 2 * n * (2 * d + d // 2 * bb // 8 + 4) / td / 1e9})
+    c, bufs = setup(n_main)
+    enc, dec = parts(c, bufs)
+    for _ in range(max(1, a.warmup)):
+        enc()
+        dec()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        enc()
+        dec()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    main_row = next(r for r in rows_sweep if r["N"] == n_main)
+    flops = 4.0 * n_main * (d // 2) * 2 * n
+    te = main_row["encode_us"] * 1e-6
+    roof = {"kernel": "encode_vq_kernel<128,5,_Float16>", "bound": "alu",
+            "achieved": flops / te / 1e12, "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": flops / te / 1e12 / FP32_VECTOR_PEAK_TFLOPS, "traffic": None}
+    res = {
+        "metric": "KV vectors encoded/s and decode-attention GB/s over packed codes (% of HBM peak)",
+        "value": 2 * n / (wall / a.steps), "unit": "vectors/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": wall / a.steps * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "fibquant k=2 round trip: GQA decode K and V (8 KV heads x 32768 "
+                               "tokens x d128, fp16 Student-t(3), 4 outlier channels x20), N=%d "
+                               "(%.1f bits per coordinate), encode + decode to fp16" %
+                               (n_main, np.log2(n_main) / 2),
+                   "vectors_per_step": 2 * n},
+        "sweep": rows_sweep, "roofline": roof,
+    }
+    if not a.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_fibquant(w, n_main)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline_fibquant(w, n_codes, rows=65536):
+    """The fp64 numpy oracle on a bounded sample: encode + decode of the first
+    `rows` keys and `rows` values (codebook built beforehand, untimed)."""
+    import oracle
+    d = 128
+    code = oracle.fibquant_codebook(d, n_codes)
+    flip = w["codec"].flip
+    k = w["k"].reshape(-1, d)[:rows].astype(np.float64)
+    v = w["v"].reshape(-1, d)[:rows].astype(np.float64)
+    t0 = time.perf_counter()
+    for x in (k, v):
+        for a in range(0, rows, 4096):
+            idx, nu, _ = oracle.encode_vq(x[a:a + 4096], flip, code)
+            oracle.decode_vq(idx, nu, flip, code)
+    dt = time.perf_counter() - t0
+    return {"value": 2 * rows / dt, "unit": "vectors/s", "cores": _threads(), "kind": "oracle",
+            "seconds": dt, "sample": "encode + decode of %d keys and %d values at N=%d "
+                                     "(fp64 numpy, blocks of 4096 rows)" % (rows, rows, n_codes)}
 
 
 def cpu_baseline_search(p, data, rows=65536, queries=16):

@@ -173,6 +173,57 @@ int tq_encode_kv(const tq_codec* kc, const tq_codec* vc, const void* k,
 int tq_decode_kv(const tq_codec* c, const tq_packed* in, int64_t n_rows, void* out,
                  int out_dtype, tq_stream_t stream);
 
+/* ---- FibQuant k = 2: vector code on 2-coordinate blocks -------------------
+ * "FibQuant", sections 2.1-2.3: the same normalise-rotate interface, but
+ * each block (z_2j, z_2j+1) of the rotated unit vector is coded as the index
+ * of its nearest codeword in one shared N-point code on the unit disk, at
+ * b = log2(N) / 2 bits per coordinate (N = 2^1 .. 2^8: b = 0.5 .. 4, half-bit
+ * steps).  Row j stores d/2 block codes of log2(N) bits in one LSB-first
+ * stream at byte j * (d/2) * log2(N) / 8, and its norm. */
+#define TQ_VQ_MAX_CODES 256
+
+/* The N x 2 codebook for dimension d (host, fp64, deterministic): radii by
+ * Bennett-Gersho companding of the block density (d-2)/(2 pi) (1-|y|^2)^((d-4)/2),
+ * r_n^2 = 1 - (1 - (n + 1/2)/N)^(4/d); angles n times the golden angle
+ * (planar Fibonacci spiral); then Lloyd iterations on a fixed polar
+ * quadrature of the density, restarted at two spiral phases, the lower-MSE
+ * code kept.
+ *   codewords  host, 2 N doubles (x, y pairs), output
+ * Returns TQ_OK or TQ_ERR_INVALID_ARG (d < 6, N not a power of two in
+ * 2..256, null output).  Host only. */
+int tq_build_vq_codebook(int d, int n_codes, double* codewords);
+
+typedef struct tq_vq_codec {
+  int32_t d;            /* 64 or 128 on the GPU */
+  int32_t n_codes;      /* N */
+  int32_t block_bits;   /* log2 N */
+  int32_t reserved;
+  float codewords[2 * TQ_VQ_MAX_CODES];  /* first N (x, y) pairs used, fp32 */
+  uint32_t flip[TQ_MAX_D / 32];          /* as in tq_codec */
+} tq_vq_codec;
+
+/* Builds the codebook with tq_build_vq_codebook, rounds it to fp32 and fills
+ * `codec`; flip as for tq_codec_init.  Host only. */
+int tq_vq_codec_init(tq_vq_codec* codec, int d, int n_codes, const uint32_t* flip);
+
+/* Encode n_rows rows: nu = |x|, z = Pi x / nu, block code j = the nearest
+ * codeword of (z_2j, z_2j+1) (ties to the lower index).  A zero row, or one
+ * with a non-finite element, encodes as z = 0 (the latter keeps its
+ * non-finite norm).
+ *   x     device, n_rows x d of `dtype` (TQ_F16 or TQ_F32), 16-byte aligned
+ *   idx   device, n_rows x (d/2) log2(N) / 8 bytes, 4-byte aligned (output)
+ *   norm  device, n_rows floats (output)
+ * d = 64 or 128 (other d: TQ_ERR_UNSUPPORTED).  Returns TQ_OK,
+ * TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED or TQ_ERR_HIP. */
+int tq_encode_vq(const tq_vq_codec* c, const void* x, int dtype, int64_t n_rows,
+                 uint8_t* idx, float* norm, tq_stream_t stream);
+
+/* Decode: x_hat = nu * Pi^T (codewords of the row's blocks, concatenated),
+ * written as n_rows x d of out_dtype (TQ_F16 rounded toward zero, or
+ * TQ_F32) to `out` (device, 16-byte aligned). */
+int tq_decode_vq(const tq_vq_codec* c, const uint8_t* idx, const float* norm, int64_t n_rows,
+                 void* out, int out_dtype, tq_stream_t stream);
+
 /* ---- a8..a11: attention from codes ----------------------------------------
  * For every batch b, query head h (KV head g = h / (hq / hkv)) and query a:
  *   s_j = scale * nu_j * ( <q', c_K[idx_j]> + sqrt(pi/2)/m * gamma_j *

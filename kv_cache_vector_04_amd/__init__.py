@@ -24,6 +24,7 @@ TQ_F16, TQ_F32 = 0, 1
 
 EXPORTS = ("tq_status_string", "tq_build_codebook", "tq_codec_init", "tq_encode_kv_workspace",
            "tq_encode_kv", "tq_decode_kv",
+           "tq_build_vq_codebook", "tq_vq_codec_init", "tq_encode_vq", "tq_decode_vq",
            "tq_attend_decode_workspace", "tq_attend_decode",
            "tq_inner_product_workspace", "tq_inner_product")
 
@@ -39,6 +40,12 @@ class TQCodec(ctypes.Structure):
                 ("code_bits", ctypes.c_int32), ("m", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("centroids", ctypes.c_float * 16), ("thresholds", ctypes.c_float * 16),
                 ("flip", ctypes.c_uint32 * 48), ("S", ctypes.c_void_p)]
+
+
+class TQVqCodec(ctypes.Structure):
+    _fields_ = [("d", ctypes.c_int32), ("n_codes", ctypes.c_int32), ("block_bits", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("codewords", ctypes.c_float * (2 * 256)),
+                ("flip", ctypes.c_uint32 * 48)]
 
 
 class TQPacked(ctypes.Structure):
@@ -75,6 +82,14 @@ def lib():
     L.tq_encode_kv.argtypes = [ctypes.POINTER(TQCodec), ctypes.POINTER(TQCodec), P, P, I, I64,
                                ctypes.POINTER(TQRope), ctypes.POINTER(TQPacked),
                                ctypes.POINTER(TQPacked), P, SZ, P]
+    L.tq_build_vq_codebook.restype = I
+    L.tq_build_vq_codebook.argtypes = [I, I, ctypes.POINTER(ctypes.c_double)]
+    L.tq_vq_codec_init.restype = I
+    L.tq_vq_codec_init.argtypes = [ctypes.POINTER(TQVqCodec), I, I, ctypes.POINTER(ctypes.c_uint32)]
+    L.tq_encode_vq.restype = I
+    L.tq_encode_vq.argtypes = [ctypes.POINTER(TQVqCodec), P, I, I64, P, P, P]
+    L.tq_decode_vq.restype = I
+    L.tq_decode_vq.argtypes = [ctypes.POINTER(TQVqCodec), P, P, I64, P, I, P]
     L.tq_decode_kv.restype = I
     L.tq_decode_kv.argtypes = [ctypes.POINTER(TQCodec), ctypes.POINTER(TQPacked), I64, P, I, P]
     L.tq_attend_decode_workspace.restype = SZ
@@ -243,6 +258,57 @@ def encode_kv(kcodec, vcodec, k, v, rope=None, kout=None, vout=None, workspace=N
                             wbytes, _stream(stream))
     _check(st, "tq_encode_kv")
     return kout, vout
+
+
+def build_vq_codebook(d, n_codes):
+    """The library's FibQuant k = 2 codebook: (n_codes, 2) fp64."""
+    cw = (ctypes.c_double * (2 * n_codes))()
+    _check(lib().tq_build_vq_codebook(int(d), int(n_codes), cw), "tq_build_vq_codebook")
+    return np.array(cw[:], dtype=np.float64).reshape(n_codes, 2)
+
+
+class VQCodec:
+    """FibQuant k = 2 codec: N codewords on the unit disk for 2-coordinate
+    blocks, log2(N) / 2 bits per coordinate."""
+
+    def __init__(self, d, n_codes, flip):
+        self.d, self.n_codes = int(d), int(n_codes)
+        self.block_bits = int(round(np.log2(n_codes)))
+        self.struct = TQVqCodec()
+        words = flip_words(flip)
+        w = (ctypes.c_uint32 * 48)(*[int(x) for x in words])
+        _check(lib().tq_vq_codec_init(ctypes.byref(self.struct), self.d, self.n_codes, w),
+               "tq_vq_codec_init")
+
+    @property
+    def row_bytes(self):
+        return self.d // 2 * self.block_bits // 8
+
+
+def encode_vq(codec, x, idx=None, norm=None, stream=None):
+    """x: device [n, d] fp16/fp32 -> (idx [n, row_bytes] uint8, norm [n] fp32)."""
+    _device_tensor(x, "x")
+    n = x.numel() // codec.d
+    if idx is None:
+        idx = torch.empty((n, codec.row_bytes), dtype=torch.uint8, device=x.device)
+    if norm is None:
+        norm = torch.empty((n,), dtype=torch.float32, device=x.device)
+    st = lib().tq_encode_vq(ctypes.byref(codec.struct), _ptr(x), _dtype_code(x), n, _ptr(idx),
+                            _ptr(norm), _stream(stream))
+    _check(st, "tq_encode_vq")
+    return idx, norm
+
+
+def decode_vq(codec, idx, norm, n, dtype=None, out=None, stream=None):
+    """Block codes back to vectors: out [n, d] (float16 unless dtype / out say float32)."""
+    if out is None:
+        out = torch.empty((n, codec.d), dtype=dtype if dtype is not None else torch.float16,
+                          device=idx.device)
+    _device_tensor(out, "out")
+    st = lib().tq_decode_vq(ctypes.byref(codec.struct), _ptr(idx), _ptr(norm), int(n), _ptr(out),
+                            _dtype_code(out), _stream(stream))
+    _check(st, "tq_decode_vq")
+    return out
 
 
 def decode_kv(codec, pk, n, dtype=None, out=None, stream=None):

@@ -132,6 +132,45 @@ extern "C" int tq_decode_kv(const tq_codec* c, const tq_packed* in, int64_t n_ro
                                             reinterpret_cast<hipStream_t>(stream)));
 }
 
+namespace {
+
+int check_vq(const tq_vq_codec* c, int64_t n_rows) {
+  if (c == nullptr || n_rows < 0) return TQ_ERR_INVALID_ARG;
+  if (c->n_codes < 2 || c->n_codes > TQ_VQ_MAX_CODES || (c->n_codes & (c->n_codes - 1)) ||
+      (1 << c->block_bits) != c->n_codes)
+    return TQ_ERR_INVALID_ARG;
+  if (c->d != 64 && c->d != 128) return TQ_ERR_UNSUPPORTED;
+  return TQ_OK;
+}
+
+}  // namespace
+
+extern "C" int tq_encode_vq(const tq_vq_codec* c, const void* x, int dtype, int64_t n_rows,
+                            uint8_t* idx, float* norm, tq_stream_t stream) {
+  int st = check_vq(c, n_rows);
+  if (st != TQ_OK) return st;
+  if (dtype != TQ_F16 && dtype != TQ_F32) return TQ_ERR_INVALID_ARG;
+  if (n_rows == 0) return TQ_OK;
+  if (x == nullptr || idx == nullptr || norm == nullptr || !aligned(x, 16) || !aligned(idx, 4) ||
+      !aligned(norm, 4))
+    return TQ_ERR_INVALID_ARG;
+  return hip_status(tqk::launch_encode_vq(*c, x, dtype, n_rows, idx, norm,
+                                          reinterpret_cast<hipStream_t>(stream)));
+}
+
+extern "C" int tq_decode_vq(const tq_vq_codec* c, const uint8_t* idx, const float* norm,
+                            int64_t n_rows, void* out, int out_dtype, tq_stream_t stream) {
+  int st = check_vq(c, n_rows);
+  if (st != TQ_OK) return st;
+  if (out_dtype != TQ_F16 && out_dtype != TQ_F32) return TQ_ERR_INVALID_ARG;
+  if (n_rows == 0) return TQ_OK;
+  if (out == nullptr || idx == nullptr || norm == nullptr || !aligned(out, 16) || !aligned(idx, 4) ||
+      !aligned(norm, 4))
+    return TQ_ERR_INVALID_ARG;
+  return hip_status(tqk::launch_decode_vq(*c, idx, norm, n_rows, out, out_dtype,
+                                          reinterpret_cast<hipStream_t>(stream)));
+}
+
 extern "C" size_t tq_attend_decode_workspace(int batch, int n_q, int hq, int hkv,
                                              int64_t ctx, int d) {
   if (batch <= 0 || n_q <= 0 || hq <= 0 || hkv <= 0 || ctx <= 0 || d <= 0) return 0;

@@ -29,6 +29,12 @@ hipError_t launch_encode_kv(const tq_codec& kc, const tq_codec& vc, const void* 
                             int64_t n_rows, const tq_packed& kout, const tq_packed& vout,
                             hipStream_t stream);
 
+// FibQuant k = 2 block codes (vq.hip).
+hipError_t launch_encode_vq(const tq_vq_codec& c, const void* x, int dtype, int64_t n_rows, uint8_t* idx,
+                            float* norm, hipStream_t stream);
+hipError_t launch_decode_vq(const tq_vq_codec& c, const uint8_t* idx, const float* norm, int64_t n_rows,
+                            void* out, int out_dtype, hipStream_t stream);
+
 // Packed rows back to vectors (materialize.hip): n_rows x d of out_dtype.
 hipError_t launch_materialize(const tq_codec& c, const tq_packed& in, int64_t n_rows, void* out,
                               int out_dtype, hipStream_t stream);

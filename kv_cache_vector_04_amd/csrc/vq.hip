@@ -1,0 +1,348 @@
+// FibQuant k = 2 on the GPU: encode rows to 2-coordinate block codes and
+// decode them back ("FibQuant", "2.3 Codifica e Decodifica").
+//
+// Both kernels use the two-lanes-per-vector layout: lane l of a wave owns
+// row 32 tile + l%32 and the coordinate half h = l/32 (coordinates
+// h d/2 .. h d/2 + d/2 - 1, blocks h d/4 .. h d/4 + d/4 - 1).
+//
+// Encode: nu^2 from the lane's half plus one exchange; D, then H_d as
+// butterflies over the lane's coordinates and one v_permlane32_swap per
+// coordinate for the stage across the halves; z = y / (sqrt(d) nu).  The
+// nearest codeword of block (z_2j, z_2j+1) maximizes <y, c_n> - |c_n|^2 / 2
+// (ties keep the lower n).  The codewords are lane-uniform: they stream from
+// the kernel arguments through scalar loads, with no LDS.
+// Decode: codewords from an LDS copy of the table, then the same
+// butterflies, D and nu / sqrt(d).
+//
+// A lane's half row holds (d/4) log2(N) bits: whole 32-bit words at d = 128,
+// whole 16-bit units at d = 64 (its start is only 2-byte aligned for odd
+// log2 N), so the store and load unit is chosen per shape.
+
+#include <cmath>
+
+#include "device_common.hpp"
+#include "internal.hpp"
+
+namespace tqk {
+
+constexpr int kVqWaves = 4;
+
+struct VqParams {
+  const void* x;
+  uint8_t* idx;
+  float* norm;
+  void* out;
+  const uint8_t* idx_in;
+  const float* norm_in;
+  int64_t n_rows;
+  float inv_sqrt_d;
+  uint32_t flip[4];
+  float codewords[2 * TQ_VQ_MAX_CODES];
+  float half_sq[TQ_VQ_MAX_CODES];   // -|c_n|^2 / 2
+};
+static_assert(sizeof(VqParams) <= 4096, "kernel argument segment");
+
+// the lane's half row of block codes: HB bytes in 32-bit words (HB % 4 == 0)
+// or 16-bit units
+template <int HB>
+struct HalfRowIO {
+  static constexpr bool kWords = HB % 4 == 0;
+  static constexpr int kUnits = kWords ? HB / 4 : HB / 2;
+  static constexpr int kUnitBits = kWords ? 32 : 16;
+};
+
+template <int HB>
+__device__ __forceinline__ void store_half_row(uint8_t* dst, const uint32_t (&bits)[(HB + 3) / 4]) {
+  using IO = HalfRowIO<HB>;
+  if constexpr (IO::kWords) {
+#pragma unroll
+    for (int j = 0; j < IO::kUnits; ++j) reinterpret_cast<uint32_t*>(dst)[j] = bits[j];
+  } else {
+#pragma unroll
+    for (int j = 0; j < IO::kUnits; ++j)
+      reinterpret_cast<uint16_t*>(dst)[j] = (uint16_t)(bits[j >> 1] >> (16 * (j & 1)));
+  }
+}
+
+template <int HB>
+__device__ __forceinline__ void load_half_row(const uint8_t* src, uint32_t (&bits)[(HB + 3) / 4]) {
+  using IO = HalfRowIO<HB>;
+#pragma unroll
+  for (int j = 0; j < (HB + 3) / 4; ++j) bits[j] = 0u;
+  if constexpr (IO::kWords) {
+#pragma unroll
+    for (int j = 0; j < IO::kUnits; ++j) bits[j] = reinterpret_cast<const uint32_t*>(src)[j];
+  } else {
+#pragma unroll
+    for (int j = 0; j < IO::kUnits; ++j)
+      bits[j >> 1] |= (uint32_t)reinterpret_cast<const uint16_t*>(src)[j] << (16 * (j & 1));
+  }
+}
+
+// H_d over the two lanes of a row: in-lane stages, then across the halves
+template <int HALF>
+__device__ __forceinline__ void wht_two_lanes(float (&w)[HALF], int h) {
+#pragma unroll
+  for (int hh = 1; hh < HALF; hh <<= 1) {
+#pragma unroll
+    for (int i = 0; i < HALF; ++i) {
+      if ((i & hh) == 0) {
+        const float a = w[i], b = w[i + hh];
+        w[i] = a + b;
+        w[i + hh] = a - b;
+      }
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  const float sgn = h ? -1.f : 1.f;
+#pragma unroll
+  for (int i = 0; i < HALF; ++i) {
+    // one swap of (w[i], w[i]) gives every lane the low lane's value in a
+    // and the high lane's in b
+    uint32_t a = __float_as_uint(w[i]), b = a;
+    swap_halves(a, b);
+    w[i] = fmaf(sgn, __uint_as_float(b), __uint_as_float(a));
+    if ((i & 15) == 15) __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <int D, int B, typename T>
+__global__ __launch_bounds__(kVqWaves * kWave, 2) void encode_vq_kernel(VqParams p) {
+  constexpr int HALF = D / 2, NBK = HALF / 2, N = 1 << B;
+  constexpr int HB = NBK * B / 8;
+  constexpr int RB = 2 * HB;                         // bytes per row
+  constexpr int HWD = (HB + 3) / 4;
+  const VqParams* kp = (const VqParams*)__builtin_amdgcn_kernarg_segment_ptr();
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane >> 5;
+  const int64_t ntiles = (p.n_rows + 31) / 32;
+  uint32_t fl[HALF / 32 > 0 ? HALF / 32 : 1];
+#pragma unroll
+  for (int j = 0; j < (HALF / 32 > 0 ? HALF / 32 : 1); ++j) fl[j] = kp->flip[(HALF * h) / 32 + j];
+
+  for (int64_t tile = (int64_t)blockIdx.x * kVqWaves + wave; tile < ntiles;
+       tile += (int64_t)gridDim.x * kVqWaves) {
+    int64_t row = tile * 32 + (lane & 31);
+    const bool valid = row < p.n_rows;
+    if (!valid) row = p.n_rows - 1;     // a lane's row reaches only its own outputs
+    float w[HALF];
+    const T* src = reinterpret_cast<const T*>(p.x) + row * D + h * HALF;
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int q = 0; q < HALF / 8; ++q) {
+        const uint4 u = reinterpret_cast<const uint4*>(src)[q];
+        const uint32_t uw[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          w[8 * q + 2 * e] = (float)__builtin_bit_cast(_Float16, (uint16_t)(uw[e] & 0xFFFFu));
+          w[8 * q + 2 * e + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(uw[e] >> 16));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < HALF / 4; ++q) {
+        const float4 u = reinterpret_cast<const float4*>(src)[q];
+        w[4 * q] = u.x; w[4 * q + 1] = u.y; w[4 * q + 2] = u.z; w[4 * q + 3] = u.w;
+      }
+    }
+    float s2 = 0.f;
+#pragma unroll
+    for (int i = 0; i < HALF; ++i) s2 = fmaf(w[i], w[i], s2);
+    uint32_t sa = __float_as_uint(s2), sb = sa;
+    swap_halves(sa, sb);
+    const float nu2 = __uint_as_float(sa) + __uint_as_float(sb);
+    const bool finite = nu2 <= 3.0e38f;
+    const float nu = sqrtf(nu2);
+    const float inv = (finite && nu > 0.f) ? p.inv_sqrt_d / nu : 0.f;
+    // D (sign bit from the flip bit), then H_d
+#pragma unroll
+    for (int i = 0; i < HALF; ++i)
+      w[i] = __uint_as_float(__float_as_uint(w[i]) ^ ((fl[i >> 5] << (31 - (i & 31))) & 0x80000000u));
+    wht_two_lanes<HALF>(w, h);
+    // a non-finite row becomes z = 0 (inf * 0 would be NaN)
+#pragma unroll
+    for (int i = 0; i < HALF; ++i) w[i] = finite ? w[i] * inv : 0.f;
+    // nearest codeword per block: argmax <y, c_n> - |c_n|^2 / 2
+    int best[NBK];
+    float bs[NBK];
+#pragma unroll
+    for (int j = 0; j < NBK; ++j) {
+      best[j] = 0;
+      bs[j] = -INFINITY;
+    }
+#pragma unroll 1
+    for (int n = 0; n < N; ++n) {
+      const float cx = kp->codewords[2 * n], cy = kp->codewords[2 * n + 1], hq = kp->half_sq[n];
+#pragma unroll
+      for (int j = 0; j < NBK; ++j) {
+        const float s = fmaf(w[2 * j + 1], cy, fmaf(w[2 * j], cx, hq));
+        const bool up = s > bs[j];
+        bs[j] = up ? s : bs[j];
+        best[j] = up ? n : best[j];
+      }
+    }
+    uint32_t bits[HWD];
+#pragma unroll
+    for (int j = 0; j < HWD; ++j) bits[j] = 0u;
+#pragma unroll
+    for (int j = 0; j < NBK; ++j) {
+      const int off = j * B, wd = off >> 5, sh = off & 31;
+      bits[wd] |= (uint32_t)best[j] << sh;
+      if (sh + B > 32) bits[wd + 1] |= (uint32_t)best[j] >> (32 - sh);
+    }
+    if (valid) {
+      store_half_row<HB>(p.idx + row * RB + h * HB, bits);
+      if (h == 0) p.norm[row] = finite ? nu : nu2;
+    }
+  }
+}
+
+template <int D, int B, bool F16>
+__global__ __launch_bounds__(kVqWaves * kWave, 2) void decode_vq_kernel(VqParams p) {
+  constexpr int HALF = D / 2, NBK = HALF / 2, N = 1 << B;
+  constexpr int HB = NBK * B / 8;
+  constexpr int RB = 2 * HB;
+  constexpr int HWD = (HB + 3) / 4;
+  __shared__ float2 s_cw[N];
+  const VqParams* kp = (const VqParams*)__builtin_amdgcn_kernarg_segment_ptr();
+  for (int n = threadIdx.x; n < N; n += blockDim.x)
+    s_cw[n] = make_float2(kp->codewords[2 * n], kp->codewords[2 * n + 1]);
+  __syncthreads();
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane >> 5;
+  const int64_t ntiles = (p.n_rows + 31) / 32;
+  uint32_t fl[HALF / 32 > 0 ? HALF / 32 : 1];
+#pragma unroll
+  for (int j = 0; j < (HALF / 32 > 0 ? HALF / 32 : 1); ++j) fl[j] = kp->flip[(HALF * h) / 32 + j];
+
+  for (int64_t tile = (int64_t)blockIdx.x * kVqWaves + wave; tile < ntiles;
+       tile += (int64_t)gridDim.x * kVqWaves) {
+    int64_t row = tile * 32 + (lane & 31);
+    const bool valid = row < p.n_rows;
+    if (!valid) row = p.n_rows - 1;
+    uint32_t bits[HWD];
+    load_half_row<HB>(p.idx_in + row * RB + h * HB, bits);
+    float w[HALF];
+#pragma unroll
+    for (int j = 0; j < NBK; ++j) {
+      const int off = j * B, wd = off >> 5, sh = off & 31;
+      uint32_t c = bits[wd] >> sh;
+      if (sh + B > 32) c |= bits[wd + 1] << (32 - sh);
+      const float2 cw = s_cw[c & (N - 1)];
+      w[2 * j] = cw.x;
+      w[2 * j + 1] = cw.y;
+      if ((j & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+    }
+    wht_two_lanes<HALF>(w, h);
+    // D and nu / sqrt(d): the scale is >= 0, its sign bit becomes the flip bit
+    const float sc = p.norm_in[row] * p.inv_sqrt_d;
+#pragma unroll
+    for (int i = 0; i < HALF; ++i)
+      w[i] *= __uint_as_float(((fl[i >> 5] << (31 - (i & 31))) & 0x80000000u) | __float_as_uint(sc));
+    if (valid) {
+      if constexpr (F16) {
+        _Float16* dst = reinterpret_cast<_Float16*>(p.out) + row * D + h * HALF;
+#pragma unroll
+        for (int q = 0; q < HALF / 8; ++q) {
+          uint32_t o[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            o[j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(w[8 * q + 2 * j], w[8 * q + 2 * j + 1]));
+          reinterpret_cast<uint4*>(dst)[q] = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+      } else {
+        float* dst = reinterpret_cast<float*>(p.out) + row * D + h * HALF;
+#pragma unroll
+        for (int q = 0; q < HALF / 4; ++q)
+          reinterpret_cast<float4*>(dst)[q] = make_float4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
+      }
+    }
+  }
+}
+
+template <typename K>
+static int64_t vq_blocks(K kernel, int64_t n_rows) {
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, kVqWaves * kWave, 0) != hipSuccess || nb < 1)
+    nb = 1;
+  const int64_t ntiles = (n_rows + 31) / 32;
+  int64_t blocks = (ntiles + kVqWaves - 1) / kVqWaves;
+  const int64_t cap = (int64_t)device_cu_count() * nb;
+  if (blocks > cap) blocks = cap;
+  return blocks < 1 ? 1 : blocks;
+}
+
+template <int D, int B>
+static hipError_t run_vq(bool encode, int dtype, const VqParams& p, hipStream_t s) {
+  if (encode) {
+    if (dtype == TQ_F16) {
+      hipLaunchKernelGGL((encode_vq_kernel<D, B, _Float16>), dim3((unsigned)vq_blocks(encode_vq_kernel<D, B, _Float16>, p.n_rows)),
+                         dim3(kVqWaves * kWave), 0, s, p);
+    } else {
+      hipLaunchKernelGGL((encode_vq_kernel<D, B, float>), dim3((unsigned)vq_blocks(encode_vq_kernel<D, B, float>, p.n_rows)),
+                         dim3(kVqWaves * kWave), 0, s, p);
+    }
+  } else {
+    if (dtype == TQ_F16) {
+      hipLaunchKernelGGL((decode_vq_kernel<D, B, true>), dim3((unsigned)vq_blocks(decode_vq_kernel<D, B, true>, p.n_rows)),
+                         dim3(kVqWaves * kWave), 0, s, p);
+    } else {
+      hipLaunchKernelGGL((decode_vq_kernel<D, B, false>), dim3((unsigned)vq_blocks(decode_vq_kernel<D, B, false>, p.n_rows)),
+                         dim3(kVqWaves * kWave), 0, s, p);
+    }
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t pick_vq(int b, bool encode, int dtype, const VqParams& p, hipStream_t s) {
+  switch (b) {
+    case 1: return run_vq<D, 1>(encode, dtype, p, s);
+    case 2: return run_vq<D, 2>(encode, dtype, p, s);
+    case 3: return run_vq<D, 3>(encode, dtype, p, s);
+    case 4: return run_vq<D, 4>(encode, dtype, p, s);
+    case 5: return run_vq<D, 5>(encode, dtype, p, s);
+    case 6: return run_vq<D, 6>(encode, dtype, p, s);
+    case 7: return run_vq<D, 7>(encode, dtype, p, s);
+    case 8: return run_vq<D, 8>(encode, dtype, p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+static void vq_params(const tq_vq_codec& c, int64_t n_rows, VqParams& p) {
+  p = {};
+  p.n_rows = n_rows;
+  p.inv_sqrt_d = (float)(1.0 / std::sqrt((double)c.d));
+  for (int w = 0; w < 4; ++w) p.flip[w] = c.flip[w];
+  for (int n = 0; n < 2 * c.n_codes; ++n) p.codewords[n] = c.codewords[n];
+  for (int n = 0; n < c.n_codes; ++n) {
+    const float x = c.codewords[2 * n], y = c.codewords[2 * n + 1];
+    p.half_sq[n] = -0.5f * (x * x + y * y);
+  }
+}
+
+hipError_t launch_encode_vq(const tq_vq_codec& c, const void* x, int dtype, int64_t n_rows, uint8_t* idx,
+                            float* norm, hipStream_t stream) {
+  if (n_rows == 0) return hipSuccess;
+  VqParams p;
+  vq_params(c, n_rows, p);
+  p.x = x;
+  p.idx = idx;
+  p.norm = norm;
+  if (c.d == 128) return pick_vq<128>(c.block_bits, true, dtype, p, stream);
+  if (c.d == 64) return pick_vq<64>(c.block_bits, true, dtype, p, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_vq(const tq_vq_codec& c, const uint8_t* idx, const float* norm, int64_t n_rows,
+                            void* out, int out_dtype, hipStream_t stream) {
+  if (n_rows == 0) return hipSuccess;
+  VqParams p;
+  vq_params(c, n_rows, p);
+  p.idx_in = idx;
+  p.norm_in = norm;
+  p.out = out;
+  if (c.d == 128) return pick_vq<128>(c.block_bits, false, out_dtype, p, stream);
+  if (c.d == 64) return pick_vq<64>(c.block_bits, false, out_dtype, p, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace tqk

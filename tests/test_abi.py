@@ -129,6 +129,58 @@ def test_decode_validation_before_launch(L):
     assert dec(ctypes.byref(wide), ctypes.byref(pv), 10, fake, tq.TQ_F16, None) == tq.TQ_ERR_UNSUPPORTED
 
 
+@pytest.mark.parametrize("d,n", [(6, 2), (64, 2), (64, 8), (64, 32), (128, 4), (128, 16), (128, 64)])
+def test_library_vq_codebook_matches_oracle(L, d, n):
+    from oracle import fibquant_codebook
+    assert np.max(np.abs(tq.build_vq_codebook(d, n) - fibquant_codebook(d, n))) < 1e-12
+
+
+def test_vq_codebook_and_codec_validation(L):
+    out = (ctypes.c_double * 512)()
+    for d, n in ((5, 4), (64, 3), (64, 1), (64, 512), (64, 0)):
+        assert L.tq_build_vq_codebook(d, n, out) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_build_vq_codebook(64, 4, None) == tq.TQ_ERR_INVALID_ARG
+    flip = np.zeros(64, dtype=bool)
+    flip[[1, 33]] = True
+    c = tq.VQCodec(64, 16, flip)
+    assert (c.struct.d, c.struct.n_codes, c.struct.block_bits) == (64, 16, 4)
+    assert c.struct.flip[0] == 2 and c.struct.flip[1] == 2 and c.struct.flip[2] == 0
+    want = tq.build_vq_codebook(64, 16).astype(np.float32).ravel()
+    assert np.array_equal(np.array(c.struct.codewords[:32], dtype=np.float32), want)
+    assert all(v == 0.0 for v in c.struct.codewords[32:])
+    assert c.row_bytes == 32 * 4 // 8
+    st = tq.TQVqCodec()
+    w = (ctypes.c_uint32 * 48)()
+    assert L.tq_vq_codec_init(ctypes.byref(st), 63, 16, w) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_vq_codec_init(ctypes.byref(st), 64, 12, w) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_vq_codec_init(ctypes.byref(st), 64, 16, None) == tq.TQ_ERR_INVALID_ARG
+
+
+def test_vq_encode_decode_validation_before_launch(L):
+    c = tq.VQCodec(128, 32, np.zeros(128, dtype=bool))
+    fake = ctypes.c_void_p(1 << 20)
+    cp = ctypes.byref(c.struct)
+    enc, dec = L.tq_encode_vq, L.tq_decode_vq
+    assert enc(None, fake, tq.TQ_F16, 10, fake, fake, None) == tq.TQ_ERR_INVALID_ARG
+    assert enc(cp, fake, 7, 10, fake, fake, None) == tq.TQ_ERR_INVALID_ARG
+    assert enc(cp, fake, tq.TQ_F16, -1, fake, fake, None) == tq.TQ_ERR_INVALID_ARG
+    assert enc(cp, ctypes.c_void_p((1 << 20) + 8), tq.TQ_F16, 10, fake, fake, None) == tq.TQ_ERR_INVALID_ARG
+    assert enc(cp, fake, tq.TQ_F16, 10, ctypes.c_void_p((1 << 20) + 2), fake, None) == tq.TQ_ERR_INVALID_ARG
+    assert enc(cp, fake, tq.TQ_F16, 10, fake, None, None) == tq.TQ_ERR_INVALID_ARG
+    assert enc(cp, None, tq.TQ_F16, 0, None, None, None) == tq.TQ_OK
+    assert dec(cp, fake, fake, 10, ctypes.c_void_p((1 << 20) + 4), tq.TQ_F32, None) == tq.TQ_ERR_INVALID_ARG
+    assert dec(cp, fake, fake, 10, fake, 5, None) == tq.TQ_ERR_INVALID_ARG
+    assert dec(cp, None, fake, 10, fake, tq.TQ_F32, None) == tq.TQ_ERR_INVALID_ARG
+    assert dec(cp, None, None, 0, None, tq.TQ_F32, None) == tq.TQ_OK
+    # a struct edited after init: N and log2 N out of step, or no GPU kernel for d
+    bad = tq.VQCodec(128, 32, np.zeros(128, dtype=bool))
+    bad.struct.block_bits = 4
+    assert enc(ctypes.byref(bad.struct), fake, tq.TQ_F16, 10, fake, fake, None) == tq.TQ_ERR_INVALID_ARG
+    wide = tq.VQCodec(96, 16, np.zeros(96, dtype=bool))
+    assert enc(ctypes.byref(wide.struct), fake, tq.TQ_F16, 10, fake, fake, None) == tq.TQ_ERR_UNSUPPORTED
+    assert dec(ctypes.byref(wide.struct), fake, fake, 10, fake, tq.TQ_F16, None) == tq.TQ_ERR_UNSUPPORTED
+
+
 def test_wide_encode_workspace(L):
     kw = _codec_struct(L, 1536, tq.TQ_PROD, 2)
     fake = ctypes.c_void_p(1 << 20)
