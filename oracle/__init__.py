@@ -38,6 +38,9 @@ from .codec import (encode_mse, encode_prod, decode_mse, decode_prod,
 from .rope import rope_interleaved
 from .attention import attention_from_codes, attention_materialized
 from .search import inner_product_matrix, top_k
+from .split import (outlier_permutation, effective_rate, encode_split_mse,
+                    encode_split_prod, decode_split, estimate_split,
+                    attention_split)
 from .fibquant import (block_pdf, spiral_init, quadrature, nearest, block_mse,
                        lloyd, fibquant_codebook, encode_vq, decode_vq, pack_vq,
                        unpack_vq)
@@ -52,4 +55,6 @@ __all__ = [
     "attention_materialized", "inner_product_matrix", "top_k", "block_pdf",
     "spiral_init", "quadrature", "nearest", "block_mse", "lloyd",
     "fibquant_codebook", "encode_vq", "decode_vq", "pack_vq", "unpack_vq",
+    "outlier_permutation", "effective_rate", "encode_split_mse",
+    "encode_split_prod", "decode_split", "estimate_split", "attention_split",
 ]
