@@ -51,14 +51,17 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sets", type=int, default=8)
     ap.add_argument("--workload", default="gqa_decode",
-                    choices=("gqa_decode", "llama_prefill", "esm2", "vector_search", "fibquant"),
+                    choices=("gqa_decode", "llama_prefill", "esm2", "vector_search", "fibquant",
+                             "split"),
                     help="gqa_decode (the default bench line); llama_prefill (32 layers x 8 KV "
                          "heads x 131072 tokens, 3-bit, encode + one decode step per layer); "
                          "esm2 (33 layers x 64 x 20 heads x 1024 tokens, d64, RoPE keys, 3-bit, "
                          "encode + bidirectional attention); vector_search (1e6 x d1536 encode "
                          "+ 1024-query scan with top-10); fibquant (the GQA K/V, 2 x 262144 "
                          "rows d128, through the k = 2 vector code at N = 32, 2.5 bits, "
-                         "encode + decode, with a sweep over N)")
+                         "encode + decode, with a sweep over N); split (the GQA step with "
+                         "outlier-channel split codecs, 3/2 bits = 2.5 and 4/3 = 3.5, attention "
+                         "through the materializing decoder)")
     a = ap.parse_args()
     heavy = a.workload != "gqa_decode"
     if a.steps is None:
@@ -85,6 +88,8 @@ def main():
         return bench_search(a, torch, synth, tq, dev)
     if a.workload == "fibquant":
         return bench_fibquant(a, torch, synth, tq, dev)
+    if a.workload == "split":
+        return bench_split(a, torch, synth, tq, dev)
     if a.workload in ("llama_prefill", "esm2"):
         return bench_layers(a, torch, synth, tq, dev)
     hkv, ctx, d, hq = 8, 32768, 128, 32
@@ -536,6 +541,212 @@ def bench_fibquant(a, torch, synth, tq, dev, n_main=32, sweep=(4, 16, 32, 64, 25
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_fibquant(w, n_main)
     print(json.dumps(res), flush=True)
+
+
+def split_codecs(tq, rng, b_hi, b_lo, synth):
+    """Key (prod) and value (mse) split codecs with fresh draws per half."""
+    out = []
+    for prod in (True, False):
+        halves = []
+        for b in (b_hi, b_lo):
+            dr = synth.codec_draws(rng, 64, m=64 if prod else 0)
+            halves.append(tq.Codec(64, tq.TQ_PROD if prod else tq.TQ_MSE, b, dr.flip,
+                                   dr.S if prod else None))
+        out.append(tq.SplitCodec(*halves))
+    return out
+
+
+def bench_split(a, torch, synth, tq, dev, main=(3, 2), sweep=((3, 2), (4, 3))):
+    """Outlier-channel split over the GQA decode workload (8 KV heads x 32768
+    tokens x 128, fp16 Student-t(3), four outlier channels x20 per head, 32
+    query heads).  Each head's K and V channels are ordered once by the
+    library's outlier rule on its first 4096 tokens (the offline permutation a
+    model folds into its projection weights; the queries take their KV head's
+    key order), outside the timed region.  A step: tq_encode_split of K and V
+    (two launches, one per channel half), tq_decode_split of both to fp32,
+    then softmax(q K^T / sqrt d) V per KV head with fp32 torch matmuls.  The
+    inputs rotate over `--sets` copies (more than the last-level cache); each
+    part is one HIP graph per copy, timed with HIP events over replays.
+    Quality: relMSE of the decoded K and V, the relative L2 error of the
+    score matrix q K^T and the agreement of its top token with the
+    unquantized one, beside whole-codec b = 2, 3, 4 (K prod, V mse) through
+    the same decoder."""
+    w = synth.gqa_decode()
+    hkv, ctx, d, hq = 8, 32768, 128, 32
+    G = hq // hkv
+    kk, vv, qq = w["k"].copy(), w["v"].copy(), w["q"].reshape(hq, d).copy()
+    for h in range(hkv):
+        pk = tq.outlier_order(kk[h, :4096], 64)
+        pv = tq.outlier_order(vv[h, :4096], 64)
+        kk[h], vv[h] = kk[h][:, pk], vv[h][:, pv]
+        qq[h * G:(h + 1) * G] = qq[h * G:(h + 1) * G][:, pk]
+    n = hkv * ctx
+    S = a.sets
+    k0 = torch.from_numpy(kk.reshape(n, d)).to(dev)
+    v0 = torch.from_numpy(vv.reshape(n, d)).to(dev)
+    ks = [k0.clone() for _ in range(S)]
+    vs = [v0.clone() for _ in range(S)]
+    q = torch.from_numpy(qq.astype(np.float32)).to(dev).reshape(hkv, G, d)
+    khat = torch.empty((n, d), dtype=torch.float32, device=dev)
+    vhat = torch.empty((n, d), dtype=torch.float32, device=dev)
+    kf, vf = k0.float().reshape(hkv, ctx, d), v0.float().reshape(hkv, ctx, d)
+    out = torch.empty((hkv, G, d), dtype=torch.float32, device=dev)
+
+    def attn(kx, vx):
+        # fp32 throughout (the transposed operand is an fp32 view)
+        s_ = torch.matmul(q, kx.transpose(1, 2)) * (1.0 / d ** 0.5)
+        return torch.matmul(torch.softmax(s_, dim=-1), vx)
+
+    # The x20 outlier channels make the logits span tens of units, so the
+    # softmax over 32768 tokens is close to one-hot and the attention output
+    # is mostly the value of the top token: the score matrix's error and the
+    # top-1 agreement measure the keys' effect, the relMSE of V the values'.
+    s_ref = torch.matmul(q, kf.transpose(1, 2)).double()
+
+    def quality(kh, vh):
+        kh3, vh3 = kh.float().reshape(hkv, ctx, d), vh.float().reshape(hkv, ctx, d)
+        rk = float((((kh3 - kf) ** 2).sum(-1) / (kf ** 2).sum(-1)).mean())
+        rv = float((((vh3 - vf) ** 2).sum(-1) / (vf ** 2).sum(-1)).mean())
+        sc = torch.matmul(q, kh3.transpose(1, 2)).double()
+        se = float((sc - s_ref).norm() / s_ref.norm())
+        top1 = float((sc.argmax(-1) == s_ref.argmax(-1)).double().mean())
+        return {"relmse_k": rk, "relmse_v": rv, "score_rel_l2_err": se, "top1_agreement": top1}
+
+    rng = np.random.default_rng(2024)
+    codecs = {bb: split_codecs(tq, rng, bb[0], bb[1], synth) for bb in sweep}
+    packs = {bb: [(tq.SplitPacked(codecs[bb][0], n, dev), tq.SplitPacked(codecs[bb][1], n, dev))
+                  for _ in range(S)] for bb in sweep}
+
+    def parts(bb):
+        kc, vc = codecs[bb]
+
+        def enc(j):
+            kp, vp = packs[bb][j]
+            tq.encode_split(kc, vc, ks[j], vs[j], kout=kp, vout=vp)
+
+        def dec(j):
+            kp, vp = packs[bb][j]
+            tq.decode_split(kc, kp, n, out=khat)
+            tq.decode_split(vc, vp, n, out=vhat)
+
+        def att(j):
+            out.copy_(attn(khat.reshape(hkv, ctx, d), vhat.reshape(hkv, ctx, d)))
+        return enc, dec, att
+
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        return g
+
+    reps = max(2, a.steps // S)
+
+    def time_graph(g, per):
+        g.replay()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / (reps * per)
+
+    def code_bytes(c):
+        total = 0
+        for h in (c.hi, c.lo):
+            total += 64 * h.code_bits // 8 + 4 + (64 // 8 + 4 if h.mode == tq.TQ_PROD else 0)
+        return total
+
+    rows = []
+    step_graphs = None
+    for bb in sweep:
+        enc, dec, att = parts(bb)
+        for j in range(S):          # eager warm-up (the matmul library sets up outside capture)
+            enc(j)
+            dec(j)
+            att(j)
+        torch.cuda.synchronize()
+        t = {name: time_graph(capture(lambda fn=fn: [fn(j) for j in range(S)]), S)
+             for name, fn in (("encode", enc), ("decode", dec), ("attention", att))}
+        enc(0)
+        dec(0)
+        torch.cuda.synchronize()
+        kc, vc = codecs[bb]
+        eb = n * (2 * 2 * d + code_bytes(kc) + code_bytes(vc))
+        db = n * (2 * 4 * d + code_bytes(kc) + code_bytes(vc))
+        rows.append(dict({"bits_hi": bb[0], "bits_lo": bb[1], "bits_per_channel": (bb[0] + bb[1]) / 2.0,
+                          "encode_us": t["encode"] * 1e6, "encode_GB_per_s": eb / t["encode"] / 1e9,
+                          "encode_frac_of_hbm_peak": eb / t["encode"] / 1e9 / HBM_PEAK_GBS,
+                          "decode_us": t["decode"] * 1e6, "decode_GB_per_s": db / t["decode"] / 1e9,
+                          "attention_us": t["attention"] * 1e6}, **quality(khat, vhat)))
+        if bb == main:
+            step_graphs = [capture(lambda j=j: (enc(j), dec(j), att(j))) for j in range(S)]
+    uniform = []
+    for b in (2, 3, 4):
+        kc = tq.Codec(d, tq.TQ_PROD, b, w["codec"].flip, w["codec"].S)
+        vc = tq.Codec(d, tq.TQ_MSE, b, w["codec"].flip)
+        kp, vp = tq.encode_kv(kc, vc, k0, v0)
+        tq.decode_kv(kc, kp, n, out=khat)
+        tq.decode_kv(vc, vp, n, out=vhat)
+        torch.cuda.synchronize()
+        uniform.append(dict({"bits": b}, **quality(khat, vhat)))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        step_graphs[i % S].replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    mr = next(r for r in rows if (r["bits_hi"], r["bits_lo"]) == main)
+    te = mr["encode_us"] * 1e-6
+    eb = mr["encode_GB_per_s"] * 1e9 * te
+    roof = {"kernel": "encode_kv_half_kernel<64, 2, 3> + <64, 1, 2> (one launch per channel half)",
+            "bound": "hbm", "achieved": eb / te / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": eb / te / 1e9 / HBM_PEAK_GBS, "traffic": None}
+    res = {
+        "metric": "KV vectors encoded/s and decode-attention GB/s over packed codes (% of HBM peak)",
+        "value": 2 * n / (wall / a.steps), "unit": "vectors/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": wall / a.steps * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "outlier-channel split on the GQA decode step: 8 KV heads x 32768 "
+                               "tokens x d128 fp16 Student-t(3), 4 outlier channels x20 per head, "
+                               "32 query heads; K prod / V mse at %d bits on the 64 outlier-ordered "
+                               "channels and %d on the rest (%.1f bits per channel); attention "
+                               "through tq_decode_split (fp32) + fp32 torch matmuls" %
+                               (main[0], main[1], (main[0] + main[1]) / 2.0),
+                   "vectors_per_step": 2 * n, "input_sets": S},
+        "sweep": rows, "uniform_codecs": uniform, "roofline": roof,
+    }
+    if not a.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_split(kk.reshape(n, d), vv.reshape(n, d), main)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline_split(k, v, bb, rows=262144):
+    """The fp64 numpy oracle on a bounded sample: split encode + decode of the
+    first `rows` keys (prod) and values (mse)."""
+    import oracle
+    from oracle import split as SP
+    rng = np.random.default_rng(7)
+
+    def half(bits, prod):
+        signs = rng.integers(0, 2, 64).astype(bool)
+        if prod:
+            c, t = oracle.codebook(64, bits - 1)
+            return {"signs": signs, "centroids": c, "thresholds": t, "S": rng.standard_normal((64, 64))}
+        c, t = oracle.codebook(64, bits)
+        return {"signs": signs, "centroids": c, "thresholds": t}
+    kh, kl, vh, vl = half(bb[0], True), half(bb[1], True), half(bb[0], False), half(bb[1], False)
+    t0 = time.perf_counter()
+    for a in range(0, rows, 8192):
+        ek = SP.encode_split_prod(k[a:a + 8192].astype(np.float64), 64, kh, kl)
+        ev = SP.encode_split_mse(v[a:a + 8192].astype(np.float64), 64, vh, vl)
+        SP.decode_split(ek, kh, kl)
+        SP.decode_split(ev, vh, vl)
+    dt = time.perf_counter() - t0
+    return {"value": 2 * rows / dt, "unit": "vectors/s", "cores": _threads(), "kind": "oracle",
+            "seconds": dt, "sample": "split %d/%d encode + decode of %d keys and %d values "
+                                     "(fp64 numpy, blocks of 8192)" % (bb[0], bb[1], rows, rows)}
 
 
 def cpu_baseline_fibquant(w, n_codes, rows=65536):

@@ -173,6 +173,52 @@ int tq_encode_kv(const tq_codec* kc, const tq_codec* vc, const void* k,
 int tq_decode_kv(const tq_codec* c, const tq_packed* in, int64_t n_rows, void* out,
                  int out_dtype, tq_stream_t stream);
 
+/* ---- outlier-channel split: rates between whole bits ----------------------
+ * "Google presenta TurboQuant", "Desempeño teórico y empírico": for rates
+ * between whole bits, outlier channels get more bits (e.g. 3) and the other
+ * channels fewer (e.g. 2), for an effective 2.5 or 3.5 bits per channel.
+ * A split codec is two codec instances over a channel partition: channels
+ * [0, hi.d) of every row go through `hi`, channels [hi.d, hi.d + lo.d)
+ * through `lo`, each with its own norm, sign flip, table, and (prod) S and
+ * gamma.  The partition is positional.  A caller whose outlier channels sit
+ * elsewhere applies one fixed channel permutation upstream (folded into the
+ * projection weights that produce K, V and the queries), so that the outlier
+ * channels come first; attention is unchanged by a permutation applied to
+ * both q and k.  Supported: hi.d = lo.d = 64 (rows of 128 elements), for
+ * (b_hi + b_lo) / 2 bits per channel plus the two norms: 3 + 2 -> 2.5,
+ * 4 + 3 -> 3.5.  Inner products split the same way:
+ * <q, x> = <q[0:64], x[0:64]> + <q[64:128], x[64:128]>. */
+typedef struct tq_split_codec {
+  tq_codec hi;   /* channels [0, hi.d) */
+  tq_codec lo;   /* channels [hi.d, hi.d + lo.d) */
+} tq_split_codec;
+
+/* The channel order that puts a head's outlier channels first: the d_hi
+ * channels of largest mean square over the calibration rows x (host,
+ * n_rows x d fp32, row-major), ascending, then the other channels,
+ * ascending; equal mean squares go to the lower channel.  order: host,
+ * d int32 (output).  Returns TQ_OK or TQ_ERR_INVALID_ARG.  Host only. */
+int tq_outlier_order(const float* x, int64_t n_rows, int d, int d_hi, int32_t* order);
+
+/* Encode rows of hi.d + lo.d elements, in place of two copies of the
+ * halves: the `hi` channels of each row of k with kc->hi and the `lo`
+ * channels with kc->lo, and likewise v with vc (either side may be null).
+ *   k, v        device, n_rows x 128 of `dtype` (TQ_F16 or TQ_F32), 16-byte aligned
+ *   kout, vout  arrays of two tq_packed: the hi half's planes, then the lo
+ *               half's, each sized for its own codec as for tq_encode_kv
+ * No RoPE and no workspace.  Returns TQ_OK, TQ_ERR_INVALID_ARG,
+ * TQ_ERR_UNSUPPORTED (halves other than 64 + 64) or TQ_ERR_HIP. */
+int tq_encode_split(const tq_split_codec* kc, const tq_split_codec* vc, const void* k,
+                    const void* v, int dtype, int64_t n_rows, const tq_packed* kout,
+                    const tq_packed* vout, tq_stream_t stream);
+
+/* Decode one tensor's two halves (in[0]: hi, in[1]: lo) into rows of
+ * hi.d + lo.d elements of out_dtype (TQ_F16, rounded toward zero, or
+ * TQ_F32) at `out` (device, 16-byte aligned), as tq_decode_kv does for
+ * each half. */
+int tq_decode_split(const tq_split_codec* c, const tq_packed* in, int64_t n_rows, void* out,
+                    int out_dtype, tq_stream_t stream);
+
 /* ---- FibQuant k = 2: vector code on 2-coordinate blocks -------------------
  * "FibQuant", sections 2.1-2.3: the same normalise-rotate interface, but
  * each block (z_2j, z_2j+1) of the rotated unit vector is coded as the index

@@ -23,7 +23,8 @@ TQ_MSE, TQ_PROD = 0, 1
 TQ_F16, TQ_F32 = 0, 1
 
 EXPORTS = ("tq_status_string", "tq_build_codebook", "tq_codec_init", "tq_encode_kv_workspace",
-           "tq_encode_kv", "tq_decode_kv",
+           "tq_encode_kv", "tq_decode_kv", "tq_encode_split", "tq_decode_split",
+           "tq_outlier_order",
            "tq_build_vq_codebook", "tq_vq_codec_init", "tq_encode_vq", "tq_decode_vq",
            "tq_attend_decode_workspace", "tq_attend_decode",
            "tq_inner_product_workspace", "tq_inner_product")
@@ -40,6 +41,10 @@ class TQCodec(ctypes.Structure):
                 ("code_bits", ctypes.c_int32), ("m", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("centroids", ctypes.c_float * 16), ("thresholds", ctypes.c_float * 16),
                 ("flip", ctypes.c_uint32 * 48), ("S", ctypes.c_void_p)]
+
+
+class TQSplitCodec(ctypes.Structure):
+    _fields_ = [("hi", TQCodec), ("lo", TQCodec)]
 
 
 class TQVqCodec(ctypes.Structure):
@@ -92,6 +97,13 @@ def lib():
     L.tq_decode_vq.argtypes = [ctypes.POINTER(TQVqCodec), P, P, I64, P, I, P]
     L.tq_decode_kv.restype = I
     L.tq_decode_kv.argtypes = [ctypes.POINTER(TQCodec), ctypes.POINTER(TQPacked), I64, P, I, P]
+    L.tq_outlier_order.restype = I
+    L.tq_outlier_order.argtypes = [P, I64, I, I, P]
+    L.tq_encode_split.restype = I
+    L.tq_encode_split.argtypes = [ctypes.POINTER(TQSplitCodec), ctypes.POINTER(TQSplitCodec), P, P, I,
+                                  I64, ctypes.POINTER(TQPacked), ctypes.POINTER(TQPacked), P]
+    L.tq_decode_split.restype = I
+    L.tq_decode_split.argtypes = [ctypes.POINTER(TQSplitCodec), ctypes.POINTER(TQPacked), I64, P, I, P]
     L.tq_attend_decode_workspace.restype = SZ
     L.tq_attend_decode_workspace.argtypes = [I, I, I, I, I64, I]
     L.tq_attend_decode.restype = I
@@ -323,6 +335,89 @@ def decode_kv(codec, pk, n, dtype=None, out=None, stream=None):
     st = lib().tq_decode_kv(ctypes.byref(codec.struct), ctypes.byref(pk.struct), int(n), _ptr(out),
                             _dtype_code(out), _stream(stream))
     _check(st, "tq_decode_kv")
+    return out
+
+
+class SplitCodec:
+    """Outlier-channel split: channels [0, 64) of each 128-channel row through
+    `hi` (a Codec of d = 64, more bits), channels [64, 128) through `lo`."""
+
+    def __init__(self, hi, lo):
+        if hi.d != 64 or lo.d != 64 or hi.mode != lo.mode:
+            raise ValueError("a split codec pairs two d = 64 codecs of one mode")
+        self.hi, self.lo = hi, lo
+        self.d, self.mode = 128, hi.mode
+        self.struct = TQSplitCodec(hi.struct, lo.struct)
+
+    @property
+    def bits_per_channel(self):
+        return (self.hi.bits + self.lo.bits) / 2.0
+
+
+def outlier_order(calib, d_hi):
+    """The library's outlier-first channel order for calibration rows
+    (host array n x d): int32 array of d channels."""
+    x = np.ascontiguousarray(np.asarray(calib, dtype=np.float32))
+    n, d = x.shape
+    order = np.empty(d, dtype=np.int32)
+    _check(lib().tq_outlier_order(x.ctypes.data_as(ctypes.c_void_p), n, d, int(d_hi),
+                                  order.ctypes.data_as(ctypes.c_void_p)), "tq_outlier_order")
+    return order
+
+
+class SplitPacked:
+    """The two halves' packed planes of n rows."""
+
+    def __init__(self, codec, n, device="cuda"):
+        self.n = int(n)
+        self.hi = Packed(codec.hi, n, device)
+        self.lo = Packed(codec.lo, n, device)
+        self.structs = (TQPacked * 2)(self.hi.struct, self.lo.struct)
+
+
+def encode_split(kcodec, vcodec, k, v, kout=None, vout=None, stream=None):
+    """Encode [..., 128] rows of k with the split codec kcodec and of v with
+    vcodec (either may be None).  Returns (kout, vout) SplitPacked."""
+    n = dt = None
+    for c, x in ((kcodec, k), (vcodec, v)):
+        if c is None:
+            continue
+        _device_tensor(x, "input")
+        if x.shape[-1] != 128:
+            raise ValueError("split rows hold 128 channels")
+        rows = x.numel() // 128
+        n = rows if n is None else n
+        if rows != n:
+            raise ValueError("k and v must hold the same number of rows")
+        d2 = _dtype_code(x)
+        dt = d2 if dt is None else dt
+        if d2 != dt:
+            raise ValueError("k and v must share a dtype")
+    dev = (k if kcodec is not None else v).device
+    if kcodec is not None and kout is None:
+        kout = SplitPacked(kcodec, n, dev)
+    if vcodec is not None and vout is None:
+        vout = SplitPacked(vcodec, n, dev)
+    st = lib().tq_encode_split(ctypes.byref(kcodec.struct) if kcodec else None,
+                               ctypes.byref(vcodec.struct) if vcodec else None,
+                               _ptr(k) if kcodec else None, _ptr(v) if vcodec else None, dt, n,
+                               kout.structs if kcodec else None, vout.structs if vcodec else None,
+                               _stream(stream))
+    _check(st, "tq_encode_split")
+    return kout, vout
+
+
+def decode_split(codec, pk, n, dtype=None, out=None, stream=None):
+    """Both halves back to [n, 128] rows (float16 unless dtype / out say float32)."""
+    if out is None:
+        dt = dtype if dtype is not None else torch.float16
+        out = torch.empty((n, 128), dtype=dt, device=pk.hi.idx.device)
+    _device_tensor(out, "out")
+    if out.numel() != n * 128:
+        raise ValueError("out must hold n x 128 elements")
+    st = lib().tq_decode_split(ctypes.byref(codec.struct), pk.structs, int(n), _ptr(out),
+                               _dtype_code(out), _stream(stream))
+    _check(st, "tq_decode_split")
     return out
 
 

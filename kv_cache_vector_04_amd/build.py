@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtq.so")
 
-SOURCES = ["codebook.cpp", "api.cpp", "qprep.hip", "encode.hip", "attend.hip", "decode.hip", "scan.hip", "wide.hip", "attend_mq.hip", "materialize.hip", "vq.hip", "vq_codebook.cpp"]
+SOURCES = ["codebook.cpp", "api.cpp", "qprep.hip", "encode.hip", "attend.hip", "decode.hip", "scan.hip", "wide.hip", "attend_mq.hip", "materialize.hip", "vq.hip", "vq_codebook.cpp", "split.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

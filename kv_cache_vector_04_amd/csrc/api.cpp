@@ -134,6 +134,78 @@ extern "C" int tq_decode_kv(const tq_codec* c, const tq_packed* in, int64_t n_ro
 
 namespace {
 
+// both halves 64 wide: the split of a 128-channel row
+int check_split(const tq_split_codec* c, const tq_packed* planes) {
+  int st = check_codec(&c->hi);
+  if (st != TQ_OK) return st;
+  if ((st = check_codec(&c->lo)) != TQ_OK) return st;
+  if (c->hi.d != 64 || c->lo.d != 64) return TQ_ERR_UNSUPPORTED;
+  if (planes == nullptr) return TQ_ERR_INVALID_ARG;
+  if ((st = check_planes(&c->hi, &planes[0])) != TQ_OK) return st;
+  return check_planes(&c->lo, &planes[1]);
+}
+
+}  // namespace
+
+extern "C" int tq_encode_split(const tq_split_codec* kc, const tq_split_codec* vc, const void* k,
+                               const void* v, int dtype, int64_t n_rows, const tq_packed* kout,
+                               const tq_packed* vout, tq_stream_t stream) {
+  if (kc == nullptr && vc == nullptr) return TQ_ERR_INVALID_ARG;
+  if (n_rows < 0 || (dtype != TQ_F16 && dtype != TQ_F32)) return TQ_ERR_INVALID_ARG;
+  const tq_split_codec* cs[2] = {kc, vc};
+  const void* xs[2] = {k, v};
+  const tq_packed* outs[2] = {kout, vout};
+  for (int s = 0; s < 2; ++s) {
+    if (cs[s] == nullptr) continue;
+    const int st = check_split(cs[s], outs[s]);
+    if (st != TQ_OK) return st;
+    if (xs[s] == nullptr || !aligned(xs[s], 16)) return TQ_ERR_INVALID_ARG;
+  }
+  if (n_rows == 0) return TQ_OK;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  const int64_t stride = 128;
+  const size_t esize = dtype == TQ_F16 ? 2 : 4;
+  for (int half = 0; half < 2; ++half) {
+    const tq_codec* hc[2];
+    const void* hx[2];
+    for (int s = 0; s < 2; ++s) {
+      hc[s] = cs[s] == nullptr ? nullptr : (half == 0 ? &cs[s]->hi : &cs[s]->lo);
+      hx[s] = cs[s] == nullptr ? nullptr : static_cast<const char*>(xs[s]) + half * 64 * esize;
+    }
+    if (hc[0] != nullptr && hc[1] != nullptr && tqk::encode_kv_fusable(*hc[0], *hc[1], dtype, false)) {
+      const int st = hip_status(tqk::launch_encode_kv(*hc[0], *hc[1], hx[0], hx[1], n_rows, kout[half],
+                                                      vout[half], hs, stride));
+      if (st != TQ_OK) return st;
+      continue;
+    }
+    for (int s = 0; s < 2; ++s) {
+      if (hc[s] == nullptr) continue;
+      const int st = hip_status(tqk::launch_encode(*hc[s], hx[s], dtype, n_rows, tqk::RopeHost{},
+                                                   outs[s][half], nullptr, hs, stride));
+      if (st != TQ_OK) return st;
+    }
+  }
+  return TQ_OK;
+}
+
+extern "C" int tq_decode_split(const tq_split_codec* c, const tq_packed* in, int64_t n_rows,
+                               void* out, int out_dtype, tq_stream_t stream) {
+  if (c == nullptr) return TQ_ERR_INVALID_ARG;
+  int st = check_split(c, in);
+  if (st != TQ_OK) return st;
+  if (n_rows < 0 || (out_dtype != TQ_F16 && out_dtype != TQ_F32)) return TQ_ERR_INVALID_ARG;
+  if (n_rows == 0) return TQ_OK;
+  if (out == nullptr || !aligned(out, 16)) return TQ_ERR_INVALID_ARG;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  const size_t esize = out_dtype == TQ_F16 ? 2 : 4;
+  if ((st = hip_status(tqk::launch_materialize(c->hi, in[0], n_rows, out, out_dtype, hs, 128))) != TQ_OK)
+    return st;
+  return hip_status(tqk::launch_materialize(c->lo, in[1], n_rows, static_cast<char*>(out) + 64 * esize,
+                                            out_dtype, hs, 128));
+}
+
+namespace {
+
 int check_vq(const tq_vq_codec* c, int64_t n_rows) {
   if (c == nullptr || n_rows < 0) return TQ_ERR_INVALID_ARG;
   if (c->n_codes < 2 || c->n_codes > TQ_VQ_MAX_CODES || (c->n_codes & (c->n_codes - 1)) ||

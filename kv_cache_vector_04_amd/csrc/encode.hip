@@ -48,6 +48,7 @@ constexpr float kGridRange = 1.01f;
 
 struct EncodeParams {
   const void* x;
+  int64_t x_stride;     // elements between consecutive rows of x (d, or more for a channel slice)
   int64_t n_rows;
   uint8_t* idx;
   uint8_t* qjl;
@@ -179,7 +180,7 @@ __global__ __launch_bounds__(kEncWaves * kWave) void encode_kernel(EncodeParams 
       if (valid) {
 #pragma unroll
         for (int j = 0; j < D / 8; ++j) {
-          const uint4 v = reinterpret_cast<const uint4*>(xin + row * D)[j];
+          const uint4 v = reinterpret_cast<const uint4*>(xin + row * p.x_stride)[j];
           u[4 * j] = v.x; u[4 * j + 1] = v.y; u[4 * j + 2] = v.z; u[4 * j + 3] = v.w;
         }
       } else {
@@ -220,7 +221,7 @@ __global__ __launch_bounds__(kEncWaves * kWave) void encode_kernel(EncodeParams 
       }
     } else {
       if (valid) {
-        load_row<D, T>(xin + row * D, x);
+        load_row<D, T>(xin + row * p.x_stride, x);
       } else {
 #pragma unroll
         for (int i = 0; i < D; ++i) x[i] = 0.f;
@@ -523,7 +524,7 @@ __device__ __forceinline__ void half_load(const EncodeParams& p, int64_t t, uint
   const int lane = threadIdx.x & 63, h = lane >> 5;
   const int64_t r = t * 32 + (lane & 31);
   if (t < (p.n_rows + 31) / 32 && r < p.n_rows) {
-    const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const _Float16*>(p.x) + r * D + h * (D / 2));
+    const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const _Float16*>(p.x) + r * p.x_stride + h * (D / 2));
 #pragma unroll
     for (int j = 0; j < NP / 4; ++j) {
       const uint4 v = src[j];
@@ -568,7 +569,7 @@ __device__ __forceinline__ void half_tiles(const EncodeParams& p, const HalfTabl
 #pragma unroll
       for (int j = 0; j < NP; ++j) u[j] = nxt[j];
     } else if (valid) {
-      const uint4* src = reinterpret_cast<const uint4*>(xin + row * D + h * HALF);
+      const uint4* src = reinterpret_cast<const uint4*>(xin + row * p.x_stride + h * HALF);
 #pragma unroll
       for (int j = 0; j < NP / 4; ++j) {
         const uint4 v = src[j];
@@ -934,9 +935,10 @@ static bool build_grid(const tq_codec& c, EncodeParams& p) {
 
 // Kernel arguments for one codec (false: no quantizer grid fits).
 static bool fill_params(const tq_codec& c, const void* x, int64_t n_rows, const RopeHost& rope,
-                        const tq_packed& out, EncodeParams& p) {
+                        const tq_packed& out, EncodeParams& p, int64_t x_stride = 0) {
   p = {};
   p.x = x;
+  p.x_stride = x_stride > 0 ? x_stride : c.d;
   p.n_rows = n_rows;
   p.idx = out.idx;
   p.qjl = out.qjl;
@@ -967,11 +969,14 @@ static bool fill_params(const tq_codec& c, const void* x, int64_t n_rows, const 
 
 hipError_t launch_encode(const tq_codec& c, const void* x, int dtype, int64_t n_rows,
                          const RopeHost& rope, const tq_packed& out, void* workspace,
-                         hipStream_t stream) {
+                         hipStream_t stream, int64_t x_stride) {
   if (n_rows == 0) return hipSuccess;
-  if (c.d == 1536) return launch_wide_encode(c, x, dtype, n_rows, out, workspace, stream);
+  if (c.d == 1536) {
+    if (x_stride != 0 && x_stride != c.d) return hipErrorInvalidValue;
+    return launch_wide_encode(c, x, dtype, n_rows, out, workspace, stream);
+  }
   EncodeParams p;
-  if (!fill_params(c, x, n_rows, rope, out, p)) return hipErrorInvalidValue;
+  if (!fill_params(c, x, n_rows, rope, out, p, x_stride)) return hipErrorInvalidValue;
   if (c.d == 128) return pick_rest<128>(c, dtype, rope.on, p, stream);
   if (c.d == 64) return pick_rest<64>(c, dtype, rope.on, p, stream);
   return hipErrorInvalidValue;
@@ -1029,10 +1034,11 @@ bool encode_kv_fusable(const tq_codec& kc, const tq_codec& vc, int dtype, bool r
 
 hipError_t launch_encode_kv(const tq_codec& kc, const tq_codec& vc, const void* k, const void* v,
                             int64_t n_rows, const tq_packed& kout, const tq_packed& vout,
-                            hipStream_t stream) {
+                            hipStream_t stream, int64_t x_stride) {
   if (n_rows == 0) return hipSuccess;
   EncodeKVParams pp;
-  if (!fill_params(kc, k, n_rows, RopeHost{}, kout, pp.k) || !fill_params(vc, v, n_rows, RopeHost{}, vout, pp.v))
+  if (!fill_params(kc, k, n_rows, RopeHost{}, kout, pp.k, x_stride) ||
+      !fill_params(vc, v, n_rows, RopeHost{}, vout, pp.v, x_stride))
     return hipErrorInvalidValue;
   if (kc.d == 128) return pick_kv<128>(kc.code_bits, vc.code_bits, pp, stream);
   return pick_kv<64>(kc.code_bits, vc.code_bits, pp, stream);

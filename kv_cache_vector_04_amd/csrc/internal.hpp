@@ -16,10 +16,12 @@ struct RopeHost {
   int64_t seq_len;
 };
 
-// Encode n_rows rows of one tensor with one codec.
+// Encode n_rows rows of one tensor with one codec.  Row j of the input
+// starts at element j * x_stride (0: c.d; d = 64 and 128 only otherwise).
 hipError_t launch_encode(const tq_codec& c, const void* x, int dtype,
                          int64_t n_rows, const RopeHost& rope,
-                         const tq_packed& out, void* workspace, hipStream_t stream);
+                         const tq_packed& out, void* workspace, hipStream_t stream,
+                         int64_t x_stride = 0);
 
 // Keys (prod) and values (mse) of one call in a single launch, for fp16
 // inputs without RoPE at d = 64 or 128 and the code widths encode_kv_fusable
@@ -27,7 +29,7 @@ hipError_t launch_encode(const tq_codec& c, const void* x, int dtype,
 bool encode_kv_fusable(const tq_codec& kc, const tq_codec& vc, int dtype, bool rope);
 hipError_t launch_encode_kv(const tq_codec& kc, const tq_codec& vc, const void* k, const void* v,
                             int64_t n_rows, const tq_packed& kout, const tq_packed& vout,
-                            hipStream_t stream);
+                            hipStream_t stream, int64_t x_stride = 0);
 
 // FibQuant k = 2 block codes (vq.hip).
 hipError_t launch_encode_vq(const tq_vq_codec& c, const void* x, int dtype, int64_t n_rows, uint8_t* idx,
@@ -35,9 +37,10 @@ hipError_t launch_encode_vq(const tq_vq_codec& c, const void* x, int dtype, int6
 hipError_t launch_decode_vq(const tq_vq_codec& c, const uint8_t* idx, const float* norm, int64_t n_rows,
                             void* out, int out_dtype, hipStream_t stream);
 
-// Packed rows back to vectors (materialize.hip): n_rows x d of out_dtype.
+// Packed rows back to vectors (materialize.hip): n_rows x d of out_dtype,
+// row j at element j * out_stride of out (0: c.d).
 hipError_t launch_materialize(const tq_codec& c, const tq_packed& in, int64_t n_rows, void* out,
-                              int out_dtype, hipStream_t stream);
+                              int out_dtype, hipStream_t stream, int64_t out_stride = 0);
 
 // d = 1536 (wide.hip).  The encode workspace holds S as fp16 hi / lo planes
 // and the residual planes of one block of vectors (prod only); the scan

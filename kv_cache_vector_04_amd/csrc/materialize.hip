@@ -40,6 +40,7 @@ struct MatParams {
   const float* norm;
   const float* rnorm;
   void* out;
+  int64_t out_stride;       // elements between consecutive output rows
   int64_t n_rows;
   float qjl_scale;          // sqrt(pi/2) / m
   float inv_sqrt_d;
@@ -204,7 +205,7 @@ __global__ __launch_bounds__(kMatWaves * kWave, MatLaunch<D>::kMinWavesPerEU) vo
     }
     if (valid) {
       if constexpr (F16) {
-        _Float16* dst = reinterpret_cast<_Float16*>(p.out) + row * D + h * HALF;
+        _Float16* dst = reinterpret_cast<_Float16*>(p.out) + row * p.out_stride + h * HALF;
 #pragma unroll
         for (int q = 0; q < HALF / 8; ++q) {
           uint32_t o[4];
@@ -214,7 +215,7 @@ __global__ __launch_bounds__(kMatWaves * kWave, MatLaunch<D>::kMinWavesPerEU) vo
           reinterpret_cast<uint4*>(dst)[q] = make_uint4(o[0], o[1], o[2], o[3]);
         }
       } else {
-        float* dst = reinterpret_cast<float*>(p.out) + row * D + h * HALF;
+        float* dst = reinterpret_cast<float*>(p.out) + row * p.out_stride + h * HALF;
 #pragma unroll
         for (int q = 0; q < HALF / 4; ++q)
           reinterpret_cast<float4*>(dst)[q] = make_float4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
@@ -262,7 +263,7 @@ static hipError_t pick_mat_d(const tq_codec& c, bool f16, const MatParams& p, hi
 }
 
 hipError_t launch_materialize(const tq_codec& c, const tq_packed& in, int64_t n_rows, void* out,
-                              int out_dtype, hipStream_t stream) {
+                              int out_dtype, hipStream_t stream, int64_t out_stride) {
   if (n_rows == 0) return hipSuccess;
   MatParams p = {};
   p.idx = in.idx;
@@ -270,6 +271,7 @@ hipError_t launch_materialize(const tq_codec& c, const tq_packed& in, int64_t n_
   p.norm = in.norm;
   p.rnorm = in.rnorm;
   p.out = out;
+  p.out_stride = out_stride > 0 ? out_stride : c.d;
   p.n_rows = n_rows;
   p.qjl_scale = c.m > 0 ? (float)(std::sqrt(M_PI / 2.0) / c.m) : 0.f;
   p.inv_sqrt_d = (float)(1.0 / std::sqrt((double)c.d));

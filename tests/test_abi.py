@@ -181,6 +181,52 @@ def test_vq_encode_decode_validation_before_launch(L):
     assert dec(ctypes.byref(wide.struct), fake, fake, 10, fake, tq.TQ_F16, None) == tq.TQ_ERR_UNSUPPORTED
 
 
+def test_outlier_order_matches_oracle(L):
+    from oracle import outlier_permutation
+    rng = np.random.default_rng(4)
+    for n, d, dh in ((100, 128, 64), (7, 16, 5), (50, 64, 0), (50, 64, 64)):
+        x = (rng.standard_t(3, (n, d)) * rng.uniform(0.5, 3, d)).astype(np.float32)
+        assert tq.outlier_order(x, dh).tolist() == outlier_permutation(x, dh).tolist()
+    # exact ties go to the lower channel
+    x = np.tile(np.array([[1, 5, 5, 0.5, 3, 3]], dtype=np.float32), (4, 1))
+    assert tq.outlier_order(x, 3).tolist() == [1, 2, 4, 0, 3, 5]
+    out = np.empty(6, dtype=np.int32)
+    ptr = out.ctypes.data_as(ctypes.c_void_p)
+    assert L.tq_outlier_order(None, 4, 6, 3, ptr) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_outlier_order(x.ctypes.data_as(ctypes.c_void_p), 4, 6, 7, ptr) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_outlier_order(x.ctypes.data_as(ctypes.c_void_p), 0, 6, 3, ptr) == tq.TQ_ERR_INVALID_ARG
+
+
+def test_split_validation_before_launch(L):
+    hi, lo = _codec_struct(L, 64, tq.TQ_PROD, 3), _codec_struct(L, 64, tq.TQ_PROD, 2)
+    sc = tq.TQSplitCodec(hi, lo)
+    vsc = tq.TQSplitCodec(_codec_struct(L, 64, tq.TQ_MSE, 3), _codec_struct(L, 64, tq.TQ_MSE, 2))
+    fake = ctypes.c_void_p(1 << 20)
+    kp = (tq.TQPacked * 2)(tq.TQPacked(1 << 20, 1 << 20, 1 << 20, 1 << 20),
+                           tq.TQPacked(1 << 20, 1 << 20, 1 << 20, 1 << 20))
+    vp = (tq.TQPacked * 2)(tq.TQPacked(1 << 20, None, 1 << 20, None), tq.TQPacked(1 << 20, None, 1 << 20, None))
+    enc, dec = L.tq_encode_split, L.tq_decode_split
+    S, V = ctypes.byref(sc), ctypes.byref(vsc)
+    assert enc(None, None, fake, fake, tq.TQ_F16, 10, kp, vp, None) == tq.TQ_ERR_INVALID_ARG
+    assert enc(S, V, fake, fake, 9, 10, kp, vp, None) == tq.TQ_ERR_INVALID_ARG
+    assert enc(S, V, fake, fake, tq.TQ_F16, -1, kp, vp, None) == tq.TQ_ERR_INVALID_ARG
+    assert enc(S, None, fake, None, tq.TQ_F16, 10, None, None, None) == tq.TQ_ERR_INVALID_ARG
+    assert enc(S, V, ctypes.c_void_p((1 << 20) + 8), fake, tq.TQ_F16, 10, kp, vp, None) == tq.TQ_ERR_INVALID_ARG
+    # prod halves need their QJL planes
+    assert enc(S, None, fake, None, tq.TQ_F16, 10, vp, None, None) == tq.TQ_ERR_INVALID_ARG
+    # halves other than 64 + 64
+    wide = tq.TQSplitCodec(_codec_struct(L, 128, tq.TQ_PROD, 3), lo)
+    assert enc(ctypes.byref(wide), None, fake, None, tq.TQ_F16, 10, kp, None, None) == tq.TQ_ERR_UNSUPPORTED
+    assert enc(S, V, None, None, tq.TQ_F32, 0, kp, vp, None) == tq.TQ_ERR_INVALID_ARG
+    assert enc(S, V, fake, fake, tq.TQ_F32, 0, kp, vp, None) == tq.TQ_OK
+    assert dec(None, kp, 10, fake, tq.TQ_F16, None) == tq.TQ_ERR_INVALID_ARG
+    assert dec(S, kp, 10, None, tq.TQ_F16, None) == tq.TQ_ERR_INVALID_ARG
+    assert dec(S, kp, 10, ctypes.c_void_p((1 << 20) + 4), tq.TQ_F32, None) == tq.TQ_ERR_INVALID_ARG
+    assert dec(S, vp, 10, fake, tq.TQ_F32, None) == tq.TQ_ERR_INVALID_ARG
+    assert dec(S, kp, 0, None, tq.TQ_F32, None) == tq.TQ_OK
+    assert dec(ctypes.byref(wide), kp, 10, fake, tq.TQ_F16, None) == tq.TQ_ERR_UNSUPPORTED
+
+
 def test_wide_encode_workspace(L):
     kw = _codec_struct(L, 1536, tq.TQ_PROD, 2)
     fake = ctypes.c_void_p(1 << 20)
