@@ -452,28 +452,51 @@ FP32_VECTOR_PEAK_TFLOPS = 157.3
 def bench_fibquant(a, torch, synth, tq, dev, n_main=32, sweep=(4, 16, 32, 64, 256)):
     """FibQuant k = 2 over the GQA decode workload's K and V (8 KV heads x
     32768 tokens x 128, fp16): a step encodes both to block codes at
-    N = 32 (2.5 bits per coordinate) and decodes both back to fp16.  Each N
-    of the sweep is timed with HIP events on the launch stream (median over
-    the steps).  The encoder's nearest search tests every codeword: 4 flops
-    (two FMAs) per (block, codeword), ALU-bound; the decoder moves
-    2 d + d/2 log2(N)/8 + 4 bytes per row."""
+    N = 32 (2.5 bits per coordinate) and decodes both back to fp16.  From
+    N = 64 up the encoder tests each block against its cell's candidate
+    codewords (the search table), below it tests all N; the sweep also times
+    the encoder that tests all N at every N.  Each
+    part of each N is one HIP graph over the `--sets` input copies, timed
+    with HIP events over replays.  Bytes per row: encode reads 2 d and
+    writes d/2 log2(N)/8 + 4; decode the reverse."""
     w = synth.gqa_decode()
     d = 128
-    k = torch.from_numpy(w["k"].reshape(-1, d)).to(dev)
-    v = torch.from_numpy(w["v"].reshape(-1, d)).to(dev)
-    n = k.shape[0]
+    S = a.sets
+    k0 = torch.from_numpy(w["k"].reshape(-1, d)).to(dev)
+    v0 = torch.from_numpy(w["v"].reshape(-1, d)).to(dev)
+    xs = [t.clone() for _ in range(S) for t in (k0, v0)]
+    n = k0.shape[0]
     flip = w["codec"].flip
+    reps = max(2, a.steps // S)
 
-    def setup(nc):
-        c = tq.VQCodec(d, nc, flip)
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        return g
+
+    def time_graph(fn, per):
+        fn()
+        torch.cuda.synchronize()
+        g = capture(fn)
+        g.replay()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / (reps * per)
+
+    def setup(nc, search=None):
+        c = tq.VQCodec(d, nc, flip, search=search)
         bufs = [(torch.empty((n, c.row_bytes), dtype=torch.uint8, device=dev),
                  torch.empty((n,), dtype=torch.float32, device=dev),
-                 torch.empty((n, d), dtype=torch.float16, device=dev)) for _ in range(2)]
-        return c, bufs
+                 torch.empty((n, d), dtype=torch.float16, device=dev)) for _ in range(2 * S)]
 
-    def parts(c, bufs):
         def enc():
-            for x, (i, nu, _) in zip((k, v), bufs):
+            for x, (i, nu, _) in zip(xs, bufs):
                 tq.encode_vq(c, x, idx=i, norm=nu)
 
         def dec():
@@ -481,61 +504,47 @@ def bench_fibquant(a, torch, synth, tq, dev, n_main=32, sweep=(4, 16, 32, 64, 25
                 tq.decode_vq(c, i, nu, n, out=o)
         return enc, dec
 
-    def timed(fns, steps):
-        for _ in range(max(1, a.warmup)):
-            for f in fns:
-                f()
-        torch.cuda.synchronize()
-        ts = [[] for _ in fns]
-        for _ in range(steps):
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
-            ev[0].record()
-            for j, f in enumerate(fns):
-                f()
-                ev[j + 1].record()
-            torch.cuda.synchronize()
-            for j in range(len(fns)):
-                ts[j].append(ev[j].elapsed_time(ev[j + 1]) * 1e-3)
-        return [float(np.median(t)) for t in ts]
-
     rows_sweep = []
+    step = None
     for nc in sweep:
-        c, bufs = setup(nc)
-        te, td = timed(parts(c, bufs), max(5, min(a.steps, 20)))
+        enc, dec = setup(nc)
+        te, td = time_graph(enc, 2 * S), time_graph(dec, 2 * S)      # per tensor
+        full_enc, _ = setup(nc, search=False)
+        tf = time_graph(full_enc, 2 * S)
         bb = int(round(np.log2(nc)))
-        rows_sweep.append({"N": nc, "bits_per_coord": bb / 2.0, "encode_us": te * 1e6,
-                           "encode_vectors_per_s": 2 * n / te,
-                           "encode_TFLOP_per_s": 4.0 * nc * (d // 2) * 2 * n / te / 1e12,
-                           "decode_us": td * 1e6,
-                           "decode_GB_per_s": 2 * n * (2 * d + d // 2 * bb // 8 + 4) / td / 1e9})
-    c, bufs = setup(n_main)
-    enc, dec = parts(c, bufs)
-    for _ in range(max(1, a.warmup)):
-        enc()
-        dec()
+        row_b = 2 * d + d // 2 * bb // 8 + 4
+        rows_sweep.append({"N": nc, "bits_per_coord": bb / 2.0,
+                           "encode_us_per_tensor": te * 1e6, "encode_GB_per_s": n * row_b / te / 1e9,
+                           "encode_full_search_us_per_tensor": tf * 1e6,
+                           "decode_us_per_tensor": td * 1e6, "decode_GB_per_s": n * row_b / td / 1e9})
+        if nc == n_main:
+            step = (enc, dec)
+    enc, dec = step
+    g_step = capture(lambda: (enc(), dec()))
+    g_step.replay()
     torch.cuda.synchronize()
+    steps = max(1, a.steps // S)
     t0 = time.perf_counter()
-    for _ in range(a.steps):
-        enc()
-        dec()
+    for _ in range(steps):
+        g_step.replay()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    wall = (time.perf_counter() - t0) / (steps * S)          # per K+V pair
     main_row = next(r for r in rows_sweep if r["N"] == n_main)
-    flops = 4.0 * n_main * (d // 2) * 2 * n
-    te = main_row["encode_us"] * 1e-6
-    roof = {"kernel": "encode_vq_kernel<128,5,_Float16>", "bound": "alu",
-            "achieved": flops / te / 1e12, "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": flops / te / 1e12 / FP32_VECTOR_PEAK_TFLOPS, "traffic": None}
+    te = main_row["encode_us_per_tensor"] * 1e-6
+    ach = main_row["encode_GB_per_s"]
+    roof = {"kernel": "encode_vq_kernel<128,5,_Float16>", "bound": "hbm",
+            "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+            "traffic": None}
     res = {
         "metric": "KV vectors encoded/s and decode-attention GB/s over packed codes (% of HBM peak)",
-        "value": 2 * n / (wall / a.steps), "unit": "vectors/s", "n_gpus": 1, "steps": a.steps,
-        "warmup": a.warmup, "ms_per_step": wall / a.steps * 1e3, "higher_is_better": True,
+        "value": 2 * n / wall, "unit": "vectors/s", "n_gpus": 1, "steps": steps * S,
+        "warmup": a.warmup, "ms_per_step": wall * 1e3, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": "fibquant k=2 round trip: GQA decode K and V (8 KV heads x 32768 "
                                "tokens x d128, fp16 Student-t(3), 4 outlier channels x20), N=%d "
                                "(%.1f bits per coordinate), encode + decode to fp16" %
                                (n_main, np.log2(n_main) / 2),
-                   "vectors_per_step": 2 * n},
+                   "vectors_per_step": 2 * n, "input_sets": S},
         "sweep": rows_sweep, "roofline": roof,
     }
     if not a.no_cpu_baseline:

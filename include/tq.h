@@ -246,11 +246,37 @@ typedef struct tq_vq_codec {
   int32_t reserved;
   float codewords[2 * TQ_VQ_MAX_CODES];  /* first N (x, y) pairs used, fp32 */
   uint32_t flip[TQ_MAX_D / 32];          /* as in tq_codec */
+  const void* search;   /* device, TQ_VQ_SEARCH_BYTES, from tq_vq_search_build; NULL: full search */
 } tq_vq_codec;
 
 /* Builds the codebook with tq_build_vq_codebook, rounds it to fp32 and fills
- * `codec`; flip as for tq_codec_init.  Host only. */
+ * `codec` (search = NULL); flip as for tq_codec_init.  Host only. */
 int tq_vq_codec_init(tq_vq_codec* codec, int d, int n_codes, const uint32_t* flip);
+
+/* The encoder's nearest-codeword search table.  Each block coordinate x is
+ * companded, u = x / (|x| + a), and a TQ_VQ_GRID^2 grid is laid uniformly
+ * over u in (-1, 1)^2: rectangular cells, narrow near 0 where the codewords
+ * crowd, the outermost reaching the unit disk's edge.  For each cell it
+ * lists, ascending, the codewords that can be nearest to some point of the
+ * cell widened on every side (by 1e-5 plus 1e-6 of the companding slope),
+ * within a score slack of 1e-5.  An empty list marks a cell for the full
+ * search (a list longer than 48, or the longest lists when all of them
+ * would overflow the TQ_VQ_ENTRIES pool).  The encoder tests a block only
+ * against its cell's list, in ascending order with strict improvement,
+ * which selects the same codeword as testing all N.  `a` is chosen per
+ * codebook (from 2^(e/2 - 1) / sqrt(d), e = 0..12) to minimize the expected
+ * number of tests on the block density.
+ * Layout: float a, float G / 2, int32 G, int32 entries used; uint16
+ * offsets[G^2 + 8] (cell k, row-major over (y cell, x cell), owns pool
+ * entries [offsets[k], offsets[k + 1])); uint8 pool[TQ_VQ_ENTRIES] of
+ * codeword indices.  tq_vq_search_build writes it for `c` into a host
+ * buffer of at least TQ_VQ_SEARCH_BYTES; the caller copies it to device
+ * memory (16-byte aligned) and sets c->search.  Returns TQ_OK or
+ * TQ_ERR_INVALID_ARG.  Host only. */
+#define TQ_VQ_GRID 64
+#define TQ_VQ_ENTRIES 24576
+#define TQ_VQ_SEARCH_BYTES (16 + 2 * (TQ_VQ_GRID * TQ_VQ_GRID + 8) + TQ_VQ_ENTRIES)
+int tq_vq_search_build(const tq_vq_codec* c, void* table, size_t bytes);
 
 /* Encode n_rows rows: nu = |x|, z = Pi x / nu, block code j = the nearest
  * codeword of (z_2j, z_2j+1) (ties to the lower index).  A zero row, or one

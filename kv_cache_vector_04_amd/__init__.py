@@ -25,7 +25,8 @@ TQ_F16, TQ_F32 = 0, 1
 EXPORTS = ("tq_status_string", "tq_build_codebook", "tq_codec_init", "tq_encode_kv_workspace",
            "tq_encode_kv", "tq_decode_kv", "tq_encode_split", "tq_decode_split",
            "tq_outlier_order",
-           "tq_build_vq_codebook", "tq_vq_codec_init", "tq_encode_vq", "tq_decode_vq",
+           "tq_build_vq_codebook", "tq_vq_codec_init", "tq_vq_search_build", "tq_encode_vq",
+           "tq_decode_vq",
            "tq_attend_decode_workspace", "tq_attend_decode",
            "tq_inner_product_workspace", "tq_inner_product")
 
@@ -50,7 +51,7 @@ class TQSplitCodec(ctypes.Structure):
 class TQVqCodec(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int32), ("n_codes", ctypes.c_int32), ("block_bits", ctypes.c_int32),
                 ("reserved", ctypes.c_int32), ("codewords", ctypes.c_float * (2 * 256)),
-                ("flip", ctypes.c_uint32 * 48)]
+                ("flip", ctypes.c_uint32 * 48), ("search", ctypes.c_void_p)]
 
 
 class TQPacked(ctypes.Structure):
@@ -91,6 +92,8 @@ def lib():
     L.tq_build_vq_codebook.argtypes = [I, I, ctypes.POINTER(ctypes.c_double)]
     L.tq_vq_codec_init.restype = I
     L.tq_vq_codec_init.argtypes = [ctypes.POINTER(TQVqCodec), I, I, ctypes.POINTER(ctypes.c_uint32)]
+    L.tq_vq_search_build.restype = I
+    L.tq_vq_search_build.argtypes = [ctypes.POINTER(TQVqCodec), P, SZ]
     L.tq_encode_vq.restype = I
     L.tq_encode_vq.argtypes = [ctypes.POINTER(TQVqCodec), P, I, I64, P, P, P]
     L.tq_decode_vq.restype = I
@@ -279,11 +282,20 @@ def build_vq_codebook(d, n_codes):
     return np.array(cw[:], dtype=np.float64).reshape(n_codes, 2)
 
 
+VQ_SEARCH_BYTES = 16 + 2 * (64 * 64 + 8) + 24576
+
+
 class VQCodec:
     """FibQuant k = 2 codec: N codewords on the unit disk for 2-coordinate
-    blocks, log2(N) / 2 bits per coordinate."""
+    blocks, log2(N) / 2 bits per coordinate.  With `search` the encoder's
+    cell table is built on the host and kept on `device` (the encoder then
+    tests each block against its cell's candidates only).  By default the
+    table is used from N = 64 up, where it is faster than testing all N
+    codewords (both give the same codes)."""
 
-    def __init__(self, d, n_codes, flip):
+    def __init__(self, d, n_codes, flip, search=None, device="cuda"):
+        if search is None:
+            search = int(n_codes) >= 64
         self.d, self.n_codes = int(d), int(n_codes)
         self.block_bits = int(round(np.log2(n_codes)))
         self.struct = TQVqCodec()
@@ -291,6 +303,15 @@ class VQCodec:
         w = (ctypes.c_uint32 * 48)(*[int(x) for x in words])
         _check(lib().tq_vq_codec_init(ctypes.byref(self.struct), self.d, self.n_codes, w),
                "tq_vq_codec_init")
+        self.search_table = None
+        self.search_dev = None
+        if search:
+            self.search_table = np.zeros(VQ_SEARCH_BYTES, dtype=np.uint8)
+            _check(lib().tq_vq_search_build(ctypes.byref(self.struct),
+                                            self.search_table.ctypes.data_as(ctypes.c_void_p),
+                                            VQ_SEARCH_BYTES), "tq_vq_search_build")
+            self.search_dev = torch.from_numpy(self.search_table).to(device)
+            self.struct.search = _ptr(self.search_dev).value
 
     @property
     def row_bytes(self):

@@ -212,6 +212,7 @@ int check_vq(const tq_vq_codec* c, int64_t n_rows) {
       (1 << c->block_bits) != c->n_codes)
     return TQ_ERR_INVALID_ARG;
   if (c->d != 64 && c->d != 128) return TQ_ERR_UNSUPPORTED;
+  if (c->search != nullptr && !aligned(c->search, 16)) return TQ_ERR_INVALID_ARG;
   return TQ_OK;
 }
 

@@ -34,6 +34,7 @@ struct VqParams {
   void* out;
   const uint8_t* idx_in;
   const float* norm_in;
+  const uint8_t* search;            // TQ_VQ_SEARCH_BYTES table or null
   int64_t n_rows;
   float inv_sqrt_d;
   uint32_t flip[4];
@@ -106,6 +107,11 @@ __device__ __forceinline__ void wht_two_lanes(float (&w)[HALF], int h) {
   }
 }
 
+constexpr int kGrid = TQ_VQ_GRID;
+constexpr int kOffsets = kGrid * kGrid + 8;                     // uint16 cell offsets
+constexpr int kTableBytes = 2 * kOffsets + TQ_VQ_ENTRIES;      // after the 16-byte header
+static_assert(kTableBytes % 16 == 0 && TQ_VQ_SEARCH_BYTES == 16 + kTableBytes, "search table layout");
+
 template <int D, int B, typename T>
 __global__ __launch_bounds__(kVqWaves * kWave, 2) void encode_vq_kernel(VqParams p) {
   constexpr int HALF = D / 2, NBK = HALF / 2, N = 1 << B;
@@ -113,6 +119,22 @@ __global__ __launch_bounds__(kVqWaves * kWave, 2) void encode_vq_kernel(VqParams
   constexpr int RB = 2 * HB;                         // bytes per row
   constexpr int HWD = (HB + 3) / 4;
   const VqParams* kp = (const VqParams*)__builtin_amdgcn_kernarg_segment_ptr();
+  // grid search: the table and the codewords in LDS
+  __shared__ uint4 s_tab[kTableBytes / 16];
+  __shared__ float4 s_cw[N];             // (x, y, -|c|^2 / 2, 0)
+  const bool grid = p.search != nullptr;
+  float grid_a = 1.f, grid_half = 0.f;
+  if (grid) {
+    const uint4* src = reinterpret_cast<const uint4*>(p.search + 16);
+    for (int i = threadIdx.x; i < kTableBytes / 16; i += blockDim.x) s_tab[i] = src[i];
+    for (int n = threadIdx.x; n < N; n += blockDim.x)
+      s_cw[n] = make_float4(kp->codewords[2 * n], kp->codewords[2 * n + 1], kp->half_sq[n], 0.f);
+    grid_a = reinterpret_cast<const float*>(p.search)[0];
+    grid_half = reinterpret_cast<const float*>(p.search)[1];
+    __syncthreads();
+  }
+  const uint16_t* s_off = reinterpret_cast<const uint16_t*>(s_tab);
+  const uint8_t* s_pool = reinterpret_cast<const uint8_t*>(s_off + kOffsets);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane >> 5;
   const int64_t ntiles = (p.n_rows + 31) / 32;
   uint32_t fl[HALF / 32 > 0 ? HALF / 32 : 1];
@@ -161,33 +183,82 @@ __global__ __launch_bounds__(kVqWaves * kWave, 2) void encode_vq_kernel(VqParams
     // a non-finite row becomes z = 0 (inf * 0 would be NaN)
 #pragma unroll
     for (int i = 0; i < HALF; ++i) w[i] = finite ? w[i] * inv : 0.f;
-    // nearest codeword per block: argmax <y, c_n> - |c_n|^2 / 2
-    int best[NBK];
-    float bs[NBK];
-#pragma unroll
-    for (int j = 0; j < NBK; ++j) {
-      best[j] = 0;
-      bs[j] = -INFINITY;
-    }
-#pragma unroll 1
-    for (int n = 0; n < N; ++n) {
-      const float cx = kp->codewords[2 * n], cy = kp->codewords[2 * n + 1], hq = kp->half_sq[n];
-#pragma unroll
-      for (int j = 0; j < NBK; ++j) {
-        const float s = fmaf(w[2 * j + 1], cy, fmaf(w[2 * j], cx, hq));
-        const bool up = s > bs[j];
-        bs[j] = up ? s : bs[j];
-        best[j] = up ? n : best[j];
-      }
-    }
+    // nearest codeword per block: argmax <y, c_n> - |c_n|^2 / 2, ties to
+    // the lower n (strict improvement in ascending order); codes packed
+    // LSB-first at B bits
     uint32_t bits[HWD];
 #pragma unroll
     for (int j = 0; j < HWD; ++j) bits[j] = 0u;
-#pragma unroll
-    for (int j = 0; j < NBK; ++j) {
+    auto put = [&](int j, int code) {
       const int off = j * B, wd = off >> 5, sh = off & 31;
-      bits[wd] |= (uint32_t)best[j] << sh;
-      if (sh + B > 32) bits[wd + 1] |= (uint32_t)best[j] >> (32 - sh);
+      bits[wd] |= (uint32_t)code << sh;
+      if (sh + B > 32) bits[wd + 1] |= (uint32_t)code >> (32 - sh);
+    };
+    if (grid) {
+      // the block's cell (companded coordinates u = x / (|x| + a), uniform
+      // grid over u) lists every codeword that can win there; an empty list:
+      // test all
+      auto axis = [&](float x) {
+        const float t = (x * __builtin_amdgcn_rcpf(fabsf(x) + grid_a) + 1.f) * grid_half;
+        return (int)fminf(fmaxf(t, 0.f), (float)(kGrid - 1));
+      };
+      // IL blocks at a time: IL independent chains of LDS reads in flight.
+      // With long lists (N >= 128) one at a time: the loop runs to the
+      // longest of the IL lists.
+      constexpr int IL = B >= 7 ? 1 : 4;
+      static_assert(NBK % IL == 0, "blocks per lane");
+#pragma unroll
+      for (int j0 = 0; j0 < NBK; j0 += IL) {
+        int beg[IL], cnt[IL], best[IL];
+        float bs[IL];
+        int iters = 0;
+#pragma unroll
+        for (int q = 0; q < IL; ++q) {
+          const int cell = axis(w[2 * (j0 + q) + 1]) * kGrid + axis(w[2 * (j0 + q)]);
+          beg[q] = s_off[cell];
+          const int c = (int)s_off[cell + 1] - beg[q];
+          cnt[q] = c == 0 ? N : c;               // an empty list: all codewords
+          beg[q] = c == 0 ? -1 : beg[q];
+          iters = max(iters, cnt[q]);
+          bs[q] = -INFINITY;
+          best[q] = 0;
+        }
+        for (int i = 0; i < iters; ++i) {
+#pragma unroll
+          for (int q = 0; q < IL; ++q) {
+            const bool on = i < cnt[q];
+            const int n = beg[q] < 0 ? i : (int)s_pool[beg[q] + (on ? i : 0)];
+            const float4 c = s_cw[n & (N - 1)];
+            const float sc = fmaf(w[2 * (j0 + q) + 1], c.y, fmaf(w[2 * (j0 + q)], c.x, c.z));
+            const bool up = on && sc > bs[q];
+            bs[q] = up ? sc : bs[q];
+            best[q] = up ? n : best[q];
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < IL; ++q) put(j0 + q, best[q]);
+      }
+    } else {
+      int best[NBK];
+      float bs[NBK];
+#pragma unroll
+      for (int j = 0; j < NBK; ++j) {
+        best[j] = 0;
+        bs[j] = -INFINITY;
+      }
+#pragma unroll 1
+      for (int n = 0; n < N; ++n) {
+        const float cx = kp->codewords[2 * n], cy = kp->codewords[2 * n + 1], hq = kp->half_sq[n];
+#pragma unroll
+        for (int j = 0; j < NBK; ++j) {
+          const float sc = fmaf(w[2 * j + 1], cy, fmaf(w[2 * j], cx, hq));
+          const bool up = sc > bs[j];
+          bs[j] = up ? sc : bs[j];
+          best[j] = up ? n : best[j];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < NBK; ++j) put(j, best[j]);
     }
     if (valid) {
       store_half_row<HB>(p.idx + row * RB + h * HB, bits);
@@ -213,13 +284,32 @@ __global__ __launch_bounds__(kVqWaves * kWave, 2) void decode_vq_kernel(VqParams
 #pragma unroll
   for (int j = 0; j < (HALF / 32 > 0 ? HALF / 32 : 1); ++j) fl[j] = kp->flip[(HALF * h) / 32 + j];
 
-  for (int64_t tile = (int64_t)blockIdx.x * kVqWaves + wave; tile < ntiles;
-       tile += (int64_t)gridDim.x * kVqWaves) {
-    int64_t row = tile * 32 + (lane & 31);
-    const bool valid = row < p.n_rows;
-    if (!valid) row = p.n_rows - 1;
+  // the next tile's codes and norm load while the current one is decoded
+  const int64_t tstride = (int64_t)gridDim.x * kVqWaves;
+  auto row_of = [&](int64_t t) {
+    const int64_t r = t * 32 + (lane & 31);
+    return r < p.n_rows ? r : p.n_rows - 1;
+  };
+  int64_t tile = (int64_t)blockIdx.x * kVqWaves + wave;
+  uint32_t nbits[HWD];
+  float nnorm = 0.f;
+  if (tile < ntiles) {
+    const int64_t r = row_of(tile);
+    load_half_row<HB>(p.idx_in + r * RB + h * HB, nbits);
+    nnorm = p.norm_in[r];
+  }
+  for (; tile < ntiles; tile += tstride) {
+    const int64_t row = row_of(tile);
+    const bool valid = tile * 32 + (lane & 31) < p.n_rows;
     uint32_t bits[HWD];
-    load_half_row<HB>(p.idx_in + row * RB + h * HB, bits);
+#pragma unroll
+    for (int j = 0; j < HWD; ++j) bits[j] = nbits[j];
+    const float norm = nnorm;
+    if (tile + tstride < ntiles) {
+      const int64_t r = row_of(tile + tstride);
+      load_half_row<HB>(p.idx_in + r * RB + h * HB, nbits);
+      nnorm = p.norm_in[r];
+    }
     float w[HALF];
 #pragma unroll
     for (int j = 0; j < NBK; ++j) {
@@ -233,7 +323,7 @@ __global__ __launch_bounds__(kVqWaves * kWave, 2) void decode_vq_kernel(VqParams
     }
     wht_two_lanes<HALF>(w, h);
     // D and nu / sqrt(d): the scale is >= 0, its sign bit becomes the flip bit
-    const float sc = p.norm_in[row] * p.inv_sqrt_d;
+    const float sc = norm * p.inv_sqrt_d;
 #pragma unroll
     for (int i = 0; i < HALF; ++i)
       w[i] *= __uint_as_float(((fl[i >> 5] << (31 - (i & 31))) & 0x80000000u) | __float_as_uint(sc));
@@ -324,6 +414,7 @@ hipError_t launch_encode_vq(const tq_vq_codec& c, const void* x, int dtype, int6
   if (n_rows == 0) return hipSuccess;
   VqParams p;
   vq_params(c, n_rows, p);
+  p.search = static_cast<const uint8_t*>(c.search);
   p.x = x;
   p.idx = idx;
   p.norm = norm;

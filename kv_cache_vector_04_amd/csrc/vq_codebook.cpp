@@ -15,8 +15,10 @@
 //     the lower-MSE result kept.  Nearest-codeword ties go to the lower
 //     index; a codeword with an empty cell stays where it is.
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <cstring>
 #include <vector>
 
 #include "tq.h"
@@ -113,7 +115,7 @@ extern "C" int tq_vq_codec_init(tq_vq_codec* codec, int d, int n_codes, const ui
   std::vector<double> cw(2 * (size_t)(n_codes > 0 ? n_codes : 1));
   const int st = tq_build_vq_codebook(d, n_codes, cw.data());
   if (st != TQ_OK) return st;
-  *codec = tq_vq_codec{};
+  *codec = tq_vq_codec{};   // search = NULL
   codec->d = d;
   codec->n_codes = n_codes;
   int b = 0;
@@ -126,5 +128,145 @@ extern "C" int tq_vq_codec_init(tq_vq_codec* codec, int d, int n_codes, const ui
     if (w == words - 1 && d % 32) m &= (1u << (d % 32)) - 1u;
     codec->flip[w] = m;
   }
+  return TQ_OK;
+}
+
+// The nearest-codeword search table (layout in tq.h).  Each block
+// coordinate is companded, u = x / (|x| + a), and the grid is uniform in u:
+// cell i of an axis holds x in [x(u_i), x(u_i+1)) with u_i = 2 i / G - 1 and
+// x(u) = a u / (1 - |u|), so cells are narrow where the codewords crowd
+// (near 0) and the outermost ones reach the disk's edge (|x| <= 1).  The
+// score of codeword c at a point p is s_c(p) = <p, c> - |c|^2 / 2; it is
+// linear in p, so over a rectangle its extremes sit at the corners.  Every
+// point of the widened cell has a best score of at least
+// L = max_c min_corners s_c, so a codeword whose largest score on the cell is
+// below L - slack can never be within slack of the best there: only the
+// others are listed.  The slack (1e-5) covers the encoder's fp32 scores.
+// Each cell edge is widened by 1e-5 plus 1e-6 dx/du at that edge: the
+// encoder's fp32 u is within a few 1e-7 of the exact one, which moves an
+// edge by that much times dx/du = a / (1 - |u|)^2 (large near |u| = 1).
+namespace {
+
+constexpr int kG = TQ_VQ_GRID;
+constexpr int kCellCap = 48;              // a longer list: full search in that cell
+constexpr int kOffsets = TQ_VQ_GRID * TQ_VQ_GRID + 8;
+
+// edge i of an axis, moved outward by its widening (side -1: lower edge of
+// a cell, +1: upper edge)
+double cell_edge(double a, int i, int side) {
+  const double u = 2.0 * i / kG - 1.0;
+  if (i <= 0) return -1.001;
+  if (i >= kG) return 1.001;
+  const double x = a * u / (1.0 - std::fabs(u));
+  const double dxdu = a / ((1.0 - std::fabs(u)) * (1.0 - std::fabs(u)));
+  return std::max(-1.001, std::min(1.001, x + side * (1e-5 + 1e-6 * dxdu)));
+}
+
+// the candidate list of every cell for companding constant a
+void fill_cells(double a, int n, const std::vector<double>& cx, const std::vector<double>& cy,
+                const std::vector<double>& hq, std::vector<std::vector<uint8_t>>& cells) {
+  constexpr double kSlack = 1e-5;
+  std::vector<double> hi(n);
+  cells.assign(kG * kG, {});
+  for (int j = 0; j < kG; ++j)
+    for (int i = 0; i < kG; ++i) {
+      const double x0 = cell_edge(a, i, -1), x1 = cell_edge(a, i + 1, 1);
+      const double y0 = cell_edge(a, j, -1), y1 = cell_edge(a, j + 1, 1);
+      const double px[4] = {x0, x1, x0, x1}, py[4] = {y0, y0, y1, y1};
+      double lo_best = -INFINITY;
+      for (int k = 0; k < n; ++k) {
+        double mn = INFINITY, mx = -INFINITY;
+        for (int q = 0; q < 4; ++q) {
+          const double sc = px[q] * cx[k] + py[q] * cy[k] + hq[k];
+          mn = std::min(mn, sc);
+          mx = std::max(mx, sc);
+        }
+        lo_best = std::max(lo_best, mn);
+        hi[k] = mx;
+      }
+      std::vector<uint8_t>& lst = cells[j * kG + i];
+      for (int k = 0; k < n; ++k)
+        if (hi[k] >= lo_best - kSlack) lst.push_back((uint8_t)k);
+      if ((int)lst.size() > kCellCap) lst.clear();      // empty: full search
+    }
+}
+
+// lists longest first into full-search cells until the pool holds the rest
+void fit_pool(std::vector<std::vector<uint8_t>>& cells) {
+  size_t total = 0;
+  for (const auto& l : cells) total += l.size();
+  while (total > (size_t)TQ_VQ_ENTRIES) {
+    size_t big = 0;
+    for (size_t k = 1; k < cells.size(); ++k)
+      if (cells[k].size() > cells[big].size()) big = k;
+    total -= cells[big].size();
+    cells[big].clear();
+  }
+}
+
+int cell_of(double a, double x) {
+  const double t = (x / (std::fabs(x) + a) + 1.0) * (kG / 2.0);
+  return std::max(0, std::min(kG - 1, (int)std::floor(t)));
+}
+
+}  // namespace
+
+extern "C" int tq_vq_search_build(const tq_vq_codec* c, void* table, size_t bytes) {
+  if (c == nullptr || table == nullptr || bytes < (size_t)TQ_VQ_SEARCH_BYTES) return TQ_ERR_INVALID_ARG;
+  const int n = c->n_codes, d = c->d;
+  if (n < 2 || n > TQ_VQ_MAX_CODES || d < 6) return TQ_ERR_INVALID_ARG;
+  std::vector<double> cx(n), cy(n), hq(n);
+  for (int i = 0; i < n; ++i) {
+    cx[i] = c->codewords[2 * i];
+    cy[i] = c->codewords[2 * i + 1];
+    hq[i] = -0.5 * (cx[i] * cx[i] + cy[i] * cy[i]);
+  }
+  // equal-weight points of the block density (rings at the Beta(1, (d-2)/2)
+  // quantiles of |y|^2) to weigh the cells by how often blocks land there
+  std::vector<double> qx, qy;
+  for (int r = 0; r < 64; ++r) {
+    const double rad = std::sqrt(1.0 - std::pow(1.0 - (r + 0.5) / 64.0, 2.0 / (d - 2)));
+    for (int t = 0; t < 64; ++t) {
+      const double th = 2.0 * M_PI * (t + 0.5) / 64.0;
+      qx.push_back(rad * std::cos(th));
+      qy.push_back(rad * std::sin(th));
+    }
+  }
+  // the companding constant with the fewest expected codeword tests per
+  // block (a full-search cell costs N), from multiples of the coordinate
+  // scale 1 / sqrt(d)
+  std::vector<std::vector<uint8_t>> cells;
+  double best_a = 0.0, best_cost = INFINITY;
+  for (int e = 0; e <= 12; ++e) {
+    const double a = std::pow(2.0, 0.5 * e - 1.0) / std::sqrt((double)d);
+    fill_cells(a, n, cx, cy, hq, cells);
+    fit_pool(cells);
+    double cost = 0.0;
+    for (size_t p = 0; p < qx.size(); ++p) {
+      const size_t k = cells[cell_of(a, qy[p]) * kG + cell_of(a, qx[p])].size();
+      cost += k == 0 ? n : (double)k;
+    }
+    if (cost < best_cost) {
+      best_cost = cost;
+      best_a = a;
+    }
+  }
+  fill_cells(best_a, n, cx, cy, hq, cells);
+  fit_pool(cells);
+  uint8_t* base = static_cast<uint8_t*>(table);
+  std::fill(base, base + TQ_VQ_SEARCH_BYTES, (uint8_t)0);
+  const float hdr_f[2] = {(float)best_a, (float)(kG / 2.0)};
+  int32_t hdr_i[2] = {kG, 0};
+  uint16_t* off = reinterpret_cast<uint16_t*>(base + 16);
+  uint8_t* pool = base + 16 + 2 * kOffsets;
+  int total = 0;
+  for (int k = 0; k < kG * kG; ++k) {
+    off[k] = (uint16_t)total;
+    for (uint8_t v : cells[k]) pool[total++] = v;
+  }
+  for (int k = kG * kG; k < kOffsets; ++k) off[k] = (uint16_t)total;
+  hdr_i[1] = total;
+  std::memcpy(base, hdr_f, 8);
+  std::memcpy(base + 8, hdr_i, 8);
   return TQ_OK;
 }

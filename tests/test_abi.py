@@ -142,7 +142,7 @@ def test_vq_codebook_and_codec_validation(L):
     assert L.tq_build_vq_codebook(64, 4, None) == tq.TQ_ERR_INVALID_ARG
     flip = np.zeros(64, dtype=bool)
     flip[[1, 33]] = True
-    c = tq.VQCodec(64, 16, flip)
+    c = tq.VQCodec(64, 16, flip, search=False)
     assert (c.struct.d, c.struct.n_codes, c.struct.block_bits) == (64, 16, 4)
     assert c.struct.flip[0] == 2 and c.struct.flip[1] == 2 and c.struct.flip[2] == 0
     want = tq.build_vq_codebook(64, 16).astype(np.float32).ravel()
@@ -157,7 +157,7 @@ def test_vq_codebook_and_codec_validation(L):
 
 
 def test_vq_encode_decode_validation_before_launch(L):
-    c = tq.VQCodec(128, 32, np.zeros(128, dtype=bool))
+    c = tq.VQCodec(128, 32, np.zeros(128, dtype=bool), search=False)
     fake = ctypes.c_void_p(1 << 20)
     cp = ctypes.byref(c.struct)
     enc, dec = L.tq_encode_vq, L.tq_decode_vq
@@ -173,58 +173,67 @@ def test_vq_encode_decode_validation_before_launch(L):
     assert dec(cp, None, fake, 10, fake, tq.TQ_F32, None) == tq.TQ_ERR_INVALID_ARG
     assert dec(cp, None, None, 0, None, tq.TQ_F32, None) == tq.TQ_OK
     # a struct edited after init: N and log2 N out of step, or no GPU kernel for d
-    bad = tq.VQCodec(128, 32, np.zeros(128, dtype=bool))
+    bad = tq.VQCodec(128, 32, np.zeros(128, dtype=bool), search=False)
     bad.struct.block_bits = 4
     assert enc(ctypes.byref(bad.struct), fake, tq.TQ_F16, 10, fake, fake, None) == tq.TQ_ERR_INVALID_ARG
-    wide = tq.VQCodec(96, 16, np.zeros(96, dtype=bool))
+    wide = tq.VQCodec(96, 16, np.zeros(96, dtype=bool), search=False)
     assert enc(ctypes.byref(wide.struct), fake, tq.TQ_F16, 10, fake, fake, None) == tq.TQ_ERR_UNSUPPORTED
     assert dec(ctypes.byref(wide.struct), fake, fake, 10, fake, tq.TQ_F16, None) == tq.TQ_ERR_UNSUPPORTED
+    # a misaligned search table
+    c.struct.search = (1 << 20) + 4
+    assert enc(cp, fake, tq.TQ_F16, 10, fake, fake, None) == tq.TQ_ERR_INVALID_ARG
 
 
-def test_outlier_order_matches_oracle(L):
-    from oracle import outlier_permutation
-    rng = np.random.default_rng(4)
-    for n, d, dh in ((100, 128, 64), (7, 16, 5), (50, 64, 0), (50, 64, 64)):
-        x = (rng.standard_t(3, (n, d)) * rng.uniform(0.5, 3, d)).astype(np.float32)
-        assert tq.outlier_order(x, dh).tolist() == outlier_permutation(x, dh).tolist()
-    # exact ties go to the lower channel
-    x = np.tile(np.array([[1, 5, 5, 0.5, 3, 3]], dtype=np.float32), (4, 1))
-    assert tq.outlier_order(x, 3).tolist() == [1, 2, 4, 0, 3, 5]
-    out = np.empty(6, dtype=np.int32)
-    ptr = out.ctypes.data_as(ctypes.c_void_p)
-    assert L.tq_outlier_order(None, 4, 6, 3, ptr) == tq.TQ_ERR_INVALID_ARG
-    assert L.tq_outlier_order(x.ctypes.data_as(ctypes.c_void_p), 4, 6, 7, ptr) == tq.TQ_ERR_INVALID_ARG
-    assert L.tq_outlier_order(x.ctypes.data_as(ctypes.c_void_p), 0, 6, 3, ptr) == tq.TQ_ERR_INVALID_ARG
+def _search_table(c):
+    buf = np.zeros(tq.VQ_SEARCH_BYTES, dtype=np.uint8)
+    assert tq.lib().tq_vq_search_build(ctypes.byref(c.struct), buf.ctypes.data_as(ctypes.c_void_p),
+                                       tq.VQ_SEARCH_BYTES) == tq.TQ_OK
+    a, half = np.frombuffer(buf[:8].tobytes(), dtype=np.float32)
+    G, used = np.frombuffer(buf[8:16].tobytes(), dtype=np.int32)
+    off = np.frombuffer(buf[16:16 + 2 * (G * G + 8)].tobytes(), dtype=np.uint16).astype(np.int64)
+    pool = buf[16 + 2 * (G * G + 8):]
+    assert off[G * G] == used <= pool.size and np.all(np.diff(off) >= 0)
+    lists = [pool[off[k]:off[k + 1]] for k in range(G * G)]
+    return np.float32(a), np.float32(half), int(G), lists
 
 
-def test_split_validation_before_launch(L):
-    hi, lo = _codec_struct(L, 64, tq.TQ_PROD, 3), _codec_struct(L, 64, tq.TQ_PROD, 2)
-    sc = tq.TQSplitCodec(hi, lo)
-    vsc = tq.TQSplitCodec(_codec_struct(L, 64, tq.TQ_MSE, 3), _codec_struct(L, 64, tq.TQ_MSE, 2))
-    fake = ctypes.c_void_p(1 << 20)
-    kp = (tq.TQPacked * 2)(tq.TQPacked(1 << 20, 1 << 20, 1 << 20, 1 << 20),
-                           tq.TQPacked(1 << 20, 1 << 20, 1 << 20, 1 << 20))
-    vp = (tq.TQPacked * 2)(tq.TQPacked(1 << 20, None, 1 << 20, None), tq.TQPacked(1 << 20, None, 1 << 20, None))
-    enc, dec = L.tq_encode_split, L.tq_decode_split
-    S, V = ctypes.byref(sc), ctypes.byref(vsc)
-    assert enc(None, None, fake, fake, tq.TQ_F16, 10, kp, vp, None) == tq.TQ_ERR_INVALID_ARG
-    assert enc(S, V, fake, fake, 9, 10, kp, vp, None) == tq.TQ_ERR_INVALID_ARG
-    assert enc(S, V, fake, fake, tq.TQ_F16, -1, kp, vp, None) == tq.TQ_ERR_INVALID_ARG
-    assert enc(S, None, fake, None, tq.TQ_F16, 10, None, None, None) == tq.TQ_ERR_INVALID_ARG
-    assert enc(S, V, ctypes.c_void_p((1 << 20) + 8), fake, tq.TQ_F16, 10, kp, vp, None) == tq.TQ_ERR_INVALID_ARG
-    # prod halves need their QJL planes
-    assert enc(S, None, fake, None, tq.TQ_F16, 10, vp, None, None) == tq.TQ_ERR_INVALID_ARG
-    # halves other than 64 + 64
-    wide = tq.TQSplitCodec(_codec_struct(L, 128, tq.TQ_PROD, 3), lo)
-    assert enc(ctypes.byref(wide), None, fake, None, tq.TQ_F16, 10, kp, None, None) == tq.TQ_ERR_UNSUPPORTED
-    assert enc(S, V, None, None, tq.TQ_F32, 0, kp, vp, None) == tq.TQ_ERR_INVALID_ARG
-    assert enc(S, V, fake, fake, tq.TQ_F32, 0, kp, vp, None) == tq.TQ_OK
-    assert dec(None, kp, 10, fake, tq.TQ_F16, None) == tq.TQ_ERR_INVALID_ARG
-    assert dec(S, kp, 10, None, tq.TQ_F16, None) == tq.TQ_ERR_INVALID_ARG
-    assert dec(S, kp, 10, ctypes.c_void_p((1 << 20) + 4), tq.TQ_F32, None) == tq.TQ_ERR_INVALID_ARG
-    assert dec(S, vp, 10, fake, tq.TQ_F32, None) == tq.TQ_ERR_INVALID_ARG
-    assert dec(S, kp, 0, None, tq.TQ_F32, None) == tq.TQ_OK
-    assert dec(ctypes.byref(wide), kp, 10, fake, tq.TQ_F16, None) == tq.TQ_ERR_UNSUPPORTED
+def _kernel_cell(x, a, half, G):
+    """The encoder's cell index of fp32 coordinates x (u = x / (|x| + a))."""
+    x = x.astype(np.float32)
+    t = (x * (np.float32(1) / (np.abs(x) + a)) + np.float32(1)) * half
+    return np.minimum(np.maximum(t, 0), G - 1).astype(np.int64)
+
+
+@pytest.mark.parametrize("d,n", [(64, 2), (64, 32), (64, 128), (128, 4), (128, 32), (128, 256)])
+def test_vq_search_table_lists_every_nearest_codeword(L, d, n):
+    """For points over the whole unit disk, dense near the codewords, and on
+    and next to the companded cell edges, the codeword nearest in fp64 is in
+    the cell list of the point's (fp32, kernel-computed) cell, or the cell is
+    marked for the full search (empty list); lists ascend with no
+    duplicates."""
+    c = tq.VQCodec(d, n, np.zeros(d, dtype=bool), search=False)
+    a, half, G, lists = _search_table(c)
+    assert G == 64 and half == G / 2
+    cw = np.array(c.struct.codewords[:2 * n], dtype=np.float32).astype(np.float64).reshape(n, 2)
+    rng = np.random.default_rng(d + n)
+    u = 2.0 * np.arange(1, G) / G - 1.0
+    edges = float(a) * u / (1.0 - np.abs(u))
+    edges = edges[np.abs(edges) < 1.0]
+    sc = 3.0 / np.sqrt(d)
+    pts = [rng.uniform(-1, 1, (60000, 2)), rng.uniform(-sc, sc, (150000, 2))]
+    e = rng.choice(edges, (40000, 1)) * (1 + rng.uniform(-3e-7, 3e-7, (40000, 1)))
+    pts.append(np.hstack([e, rng.uniform(-sc, sc, (40000, 1))]))
+    pts.append(np.hstack([rng.uniform(-sc, sc, (40000, 1)), e]))
+    p = np.vstack(pts)
+    p = p[np.hypot(p[:, 0], p[:, 1]) <= 1.0]
+    cell = _kernel_cell(p[:, 1], a, half, G) * G + _kernel_cell(p[:, 0], a, half, G)
+    near = np.argmin(((p[:, None, :] - cw[None, :, :]) ** 2).sum(-1), axis=1)
+    member = np.zeros((G * G, n), dtype=bool)
+    for k, l in enumerate(lists):
+        member[k, l] = True
+        assert np.all(np.diff(l.astype(int)) > 0)
+    full = np.array([len(l) == 0 for l in lists])[cell]
+    assert np.all(full | member[cell, near])
 
 
 def test_wide_encode_workspace(L):

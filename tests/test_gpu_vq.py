@@ -108,6 +108,39 @@ def test_vq_encode_decode_parity(d, n_codes, dtype):
     check_zero_row_codes(g[6], code)
 
 
+def adversarial_rows(rng, n, d):
+    """Gaussian and heavy-tailed rows with outlier channels, one-hot spikes,
+    constant rows, fp16 extremes, tiny norms and zero rows."""
+    x = rng.standard_normal((n, d))
+    x[: n // 4] = rng.standard_t(2, (n // 4, d))
+    x[: n // 4, [1, 9, 30]] *= 50.0
+    k = n // 4
+    x[k:k + d] = np.eye(d) * rng.uniform(0.5, 2, (d, 1))
+    x[k + d:k + d + 8] = np.sign(rng.standard_normal((8, 1))) * rng.uniform(0.1, 3, (8, 1))
+    x[k + d + 8:k + d + 12] = 65504.0 * np.sign(rng.standard_normal((4, d)))
+    x[k + d + 12:k + d + 20] *= 1e-6
+    x[k + d + 20:k + d + 23] = 0.0
+    return x
+
+
+@pytest.mark.parametrize("d,n_codes", [(64, 2), (64, 32), (64, 128), (128, 4), (128, 32), (128, 256)])
+def test_vq_grid_search_equals_full_search(d, n_codes):
+    """The encoder with the cell table writes the same bytes as the encoder
+    testing all N codewords (the table only skips codewords that cannot
+    win), on adversarial rows as well as regular ones."""
+    say("vq grid == full d=%d N=%d" % (d, n_codes))
+    rng = np.random.default_rng(40 + d + n_codes)
+    n = 32 * 200 + 19
+    flip = synth.codec_draws(rng, d).flip
+    x = torch.from_numpy(adversarial_rows(rng, n, d).astype(np.float16)).cuda()
+    grid = tq.VQCodec(d, n_codes, flip, search=True)
+    full = tq.VQCodec(d, n_codes, flip, search=False)
+    gi, gn = tq.encode_vq(grid, x)
+    fi, fn = tq.encode_vq(full, x)
+    torch.cuda.synchronize()
+    assert torch.equal(gi, fi) and torch.equal(gn, fn)
+
+
 def test_vq_non_finite_row_codes_as_zero():
     """A row with an infinite element keeps its infinite norm and gets the
     codes of z = 0, like the zero row."""
