@@ -37,8 +37,8 @@ HBM_PEAK_GBS = 8000.0
 # current kernels, scaled by the runtime copy kernel's reading on a known
 # 64 MiB copy (FETCH_SIZE x2.0, WRITE_SIZE x1.0); None where the kernel has
 # changed since the counters were taken.
-TRAFFIC = {"encode": (65959 * 2 + 35840) * 1024,
-           "attend": (18334 * 2 + 520 + 365 * 2 + 16) * 1024}
+TRAFFIC = {"encode": (65961 * 2 + 35840) * 1024,
+           "attend": (18329 * 2 + 520 + 369 * 2 + 16) * 1024}
 
 
 def parse():

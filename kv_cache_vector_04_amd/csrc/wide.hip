@@ -512,8 +512,6 @@ __global__ __launch_bounds__(64 * kSWaves, 2) void wide_scan_kernel(WScanParams 
     qb = b % QB;
     rt = b / QB;
   }
-  const int64_t qa = qb * 32 + (lane & 31);
-  const int64_t qrow = qa < p.n_q ? qa : 0;
   const int64_t r0 = rt * kSRows + wave * 32 * kSRB;
   constexpr int RB = kWD * CB / 8;
   const uint8_t* crow[kSRB];
@@ -525,11 +523,6 @@ __global__ __launch_bounds__(64 * kSWaves, 2) void wide_scan_kernel(WScanParams 
     crow[rb] = p.idx + jr * RB;
     srow[rb] = PROD ? p.qjl + jr * (kWD / 8) : nullptr;
   }
-  const _Float16* aqh = p.qh + qrow * kWD + 64 * h;
-  const _Float16* aql = p.ql + qrow * kWD + 64 * h;
-  const _Float16* ash = PROD ? p.sh + qrow * kWD + 64 * h : nullptr;
-  const _Float16* asl = PROD ? p.sl + qrow * kWD + 64 * h : nullptr;
-
   f32x16 accm[kSRB], accq[kSRB];
 #pragma unroll
   for (int rb = 0; rb < kSRB; ++rb)
