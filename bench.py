@@ -572,8 +572,10 @@ def bench_split(a, torch, synth, tq, dev, main=(3, 2), sweep=((3, 2), (4, 3))):
     library's outlier rule on its first 4096 tokens (the offline permutation a
     model folds into its projection weights; the queries take their KV head's
     key order), outside the timed region.  A step: tq_encode_split of K and V
-    (two launches, one per channel half), tq_decode_split of both to fp32,
-    then softmax(q K^T / sqrt d) V per KV head with fp32 torch matmuls.  The
+    (two launches, one per channel half), then tq_attend_split, attention of
+    the 32 query heads straight from the split codes.  The two-pass path
+    (tq_decode_split of both to fp32, then softmax(q K^T / sqrt d) V with fp32
+    torch matmuls) is timed beside it for comparison.  The
     inputs rotate over `--sets` copies (more than the last-level cache); each
     part is one HIP graph per copy, timed with HIP events over replays.
     Quality: relMSE of the decoded K and V, the relative L2 error of the
@@ -600,6 +602,9 @@ def bench_split(a, torch, synth, tq, dev, main=(3, 2), sweep=((3, 2), (4, 3))):
     vhat = torch.empty((n, d), dtype=torch.float32, device=dev)
     kf, vf = k0.float().reshape(hkv, ctx, d), v0.float().reshape(hkv, ctx, d)
     out = torch.empty((hkv, G, d), dtype=torch.float32, device=dev)
+    q4 = q.reshape(1, hq, 1, d).contiguous()
+    out4 = torch.empty((1, hq, 1, d), dtype=torch.float32, device=dev)
+    ws = torch.zeros((tq.attend_workspace_bytes(1, 1, hq, hkv, ctx, d),), dtype=torch.uint8, device=dev)
 
     def attn(kx, vx):
         # fp32 throughout (the transposed operand is an fp32 view)
@@ -640,7 +645,11 @@ def bench_split(a, torch, synth, tq, dev, main=(3, 2), sweep=((3, 2), (4, 3))):
 
         def att(j):
             out.copy_(attn(khat.reshape(hkv, ctx, d), vhat.reshape(hkv, ctx, d)))
-        return enc, dec, att
+
+        def fused(j):
+            kp, vp = packs[bb][j]
+            tq.attend_split(kc, vc, q4, kp, vp, ctx, hkv, out=out4, workspace=ws)
+        return enc, dec, att, fused
 
     def capture(fn):
         g = torch.cuda.CUDAGraph()
@@ -670,14 +679,16 @@ def bench_split(a, torch, synth, tq, dev, main=(3, 2), sweep=((3, 2), (4, 3))):
     rows = []
     step_graphs = None
     for bb in sweep:
-        enc, dec, att = parts(bb)
+        enc, dec, att, fused = parts(bb)
         for j in range(S):          # eager warm-up (the matmul library sets up outside capture)
             enc(j)
             dec(j)
             att(j)
+            fused(j)
         torch.cuda.synchronize()
         t = {name: time_graph(capture(lambda fn=fn: [fn(j) for j in range(S)]), S)
-             for name, fn in (("encode", enc), ("decode", dec), ("attention", att))}
+             for name, fn in (("encode", enc), ("decode", dec), ("attention", att),
+                              ("fused", fused))}
         enc(0)
         dec(0)
         torch.cuda.synchronize()
@@ -687,10 +698,21 @@ def bench_split(a, torch, synth, tq, dev, main=(3, 2), sweep=((3, 2), (4, 3))):
         rows.append(dict({"bits_hi": bb[0], "bits_lo": bb[1], "bits_per_channel": (bb[0] + bb[1]) / 2.0,
                           "encode_us": t["encode"] * 1e6, "encode_GB_per_s": eb / t["encode"] / 1e9,
                           "encode_frac_of_hbm_peak": eb / t["encode"] / 1e9 / HBM_PEAK_GBS,
-                          "decode_us": t["decode"] * 1e6, "decode_GB_per_s": db / t["decode"] / 1e9,
-                          "attention_us": t["attention"] * 1e6}, **quality(khat, vhat)))
+                          "attend_split_us": t["fused"] * 1e6,
+                          "attend_split_GB_per_s": n * (code_bytes(kc) + code_bytes(vc)) / t["fused"] / 1e9,
+                          "two_pass": {"decode_us": t["decode"] * 1e6,
+                                       "decode_GB_per_s": db / t["decode"] / 1e9,
+                                       "attention_us": t["attention"] * 1e6}},
+                         **quality(khat, vhat)))
+        # the fused output against the two-pass one on the same codes
+        fused(0)
+        dec(0)
+        att(0)
+        torch.cuda.synchronize()
+        rows[-1]["fused_vs_two_pass_max_row_rel_diff"] = float(
+            ((out4.reshape(hkv, G, d) - out).norm(dim=-1) / out.norm(dim=-1)).max())
         if bb == main:
-            step_graphs = [capture(lambda j=j: (enc(j), dec(j), att(j))) for j in range(S)]
+            step_graphs = [capture(lambda j=j: (enc(j), fused(j))) for j in range(S)]
     uniform = []
     for b in (2, 3, 4):
         kc = tq.Codec(d, tq.TQ_PROD, b, w["codec"].flip, w["codec"].S)
@@ -712,6 +734,10 @@ def bench_split(a, torch, synth, tq, dev, main=(3, 2), sweep=((3, 2), (4, 3))):
     roof = {"kernel": "encode_kv_half_kernel<64, 2, 3> + <64, 1, 2> (one launch per channel half)",
             "bound": "hbm", "achieved": eb / te / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": eb / te / 1e9 / HBM_PEAK_GBS, "traffic": None}
+    if mr["attend_split_us"] > mr["encode_us"]:
+        roof = {"kernel": "decode_split_kernel<2, 1, 3, 2> + merge_kernel<128>", "bound": "hbm",
+                "achieved": mr["attend_split_GB_per_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": mr["attend_split_GB_per_s"] / HBM_PEAK_GBS, "traffic": None}
     res = {
         "metric": "KV vectors encoded/s and decode-attention GB/s over packed codes (% of HBM peak)",
         "value": 2 * n / (wall / a.steps), "unit": "vectors/s", "n_gpus": 1, "steps": a.steps,
@@ -720,8 +746,8 @@ def bench_split(a, torch, synth, tq, dev, main=(3, 2), sweep=((3, 2), (4, 3))):
         "config": {"workload": "outlier-channel split on the GQA decode step: 8 KV heads x 32768 "
                                "tokens x d128 fp16 Student-t(3), 4 outlier channels x20 per head, "
                                "32 query heads; K prod / V mse at %d bits on the 64 outlier-ordered "
-                               "channels and %d on the rest (%.1f bits per channel); attention "
-                               "through tq_decode_split (fp32) + fp32 torch matmuls" %
+                               "channels and %d on the rest (%.1f bits per channel); a step is "
+                               "tq_encode_split + tq_attend_split (attention from the split codes)" %
                                (main[0], main[1], (main[0] + main[1]) / 2.0),
                    "vectors_per_step": 2 * n, "input_sets": S},
         "sweep": rows, "uniform_codecs": uniform, "roofline": roof,

@@ -323,6 +323,33 @@ int tq_attend_decode(const tq_codec* kc, const tq_codec* vc, const void* q,
                      float* scores_out, void* workspace,
                      size_t workspace_bytes, tq_stream_t stream);
 
+/* Attention from outlier-split codes: the keys and values of each token are
+ * two d = 64 codecs over channels [0, 64) and [64, 128) (tq_encode_split), so
+ *   s_j = scale * sum_h nu_hj ( <q'_h, c_Kh[idx_hj]> + sqrt(pi/2)/64 *
+ *                               gamma_hj * <S_h q'_h, 2 sigma_hj - 1> ),
+ *   q'_h = Pi_h q[h-th 64 channels],
+ *   o[h-th 64 channels] = Pi_Vh^T ( sum_j softmax(s)_j * nu^V_hj * c_Vh[idx^V_hj] )
+ * in one pass over the codes, like tq_attend_decode ("Google presenta
+ * TurboQuant", "Desempeño teórico y empírico", for the rates between whole
+ * bits; the estimator as in tq_attend_decode).
+ *   kc  split codec of the keys (TQ_PROD halves), vc of the values (TQ_MSE
+ *       halves); table widths (hi, lo) of (2, 1) or (3, 2) for the keys and
+ *       (3, 2) or (4, 3) for the values (the 2.5- and 3.5-bit points);
+ *       others: TQ_ERR_UNSUPPORTED
+ *   q   device [batch][hq][n_q][128] of `q_dtype`, channels in the codecs'
+ *       order (outlier channels first); no RoPE
+ *   k,v arrays of two tq_packed (hi, lo), rows [batch][hkv][ctx]
+ *   scale  0 selects 1/sqrt(128)
+ *   out, scores_out, workspace: as tq_attend_decode, with the workspace size
+ *       tq_attend_decode_workspace(batch, n_q, hq, hkv, ctx, 128)
+ * (hq / hkv) * n_q <= 16 (larger: TQ_ERR_UNSUPPORTED).  Returns TQ_OK,
+ * TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_WORKSPACE or TQ_ERR_HIP. */
+int tq_attend_split(const tq_split_codec* kc, const tq_split_codec* vc, const void* q,
+                    int q_dtype, int batch, int n_q, int hq, int hkv, const tq_packed* k,
+                    const tq_packed* v, int64_t ctx, float scale, float* out,
+                    float* scores_out, void* workspace, size_t workspace_bytes,
+                    tq_stream_t stream);
+
 /* ---- a12: inner-product scan (+ top-k) --------------------------------------
  * est(a, j) = nu_j ( <Pi q_a, c[idx_j]> + sqrt(pi/2)/m gamma_j
  *                    <S Pi q_a, 2 sigma_j - 1> )  (mse: first term only)

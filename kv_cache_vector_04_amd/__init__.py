@@ -23,7 +23,7 @@ TQ_MSE, TQ_PROD = 0, 1
 TQ_F16, TQ_F32 = 0, 1
 
 EXPORTS = ("tq_status_string", "tq_build_codebook", "tq_codec_init", "tq_encode_kv_workspace",
-           "tq_encode_kv", "tq_decode_kv", "tq_encode_split", "tq_decode_split",
+           "tq_encode_kv", "tq_decode_kv", "tq_encode_split", "tq_decode_split", "tq_attend_split",
            "tq_outlier_order",
            "tq_build_vq_codebook", "tq_vq_codec_init", "tq_vq_search_build", "tq_encode_vq",
            "tq_decode_vq",
@@ -102,6 +102,10 @@ def lib():
     L.tq_decode_kv.argtypes = [ctypes.POINTER(TQCodec), ctypes.POINTER(TQPacked), I64, P, I, P]
     L.tq_outlier_order.restype = I
     L.tq_outlier_order.argtypes = [P, I64, I, I, P]
+    L.tq_attend_split.restype = I
+    L.tq_attend_split.argtypes = [ctypes.POINTER(TQSplitCodec), ctypes.POINTER(TQSplitCodec), P, I, I,
+                                  I, I, I, ctypes.POINTER(TQPacked), ctypes.POINTER(TQPacked), I64,
+                                  F, P, P, P, SZ, P]
     L.tq_encode_split.restype = I
     L.tq_encode_split.argtypes = [ctypes.POINTER(TQSplitCodec), ctypes.POINTER(TQSplitCodec), P, P, I,
                                   I64, ctypes.POINTER(TQPacked), ctypes.POINTER(TQPacked), P]
@@ -439,6 +443,28 @@ def decode_split(codec, pk, n, dtype=None, out=None, stream=None):
     st = lib().tq_decode_split(ctypes.byref(codec.struct), pk.structs, int(n), _ptr(out),
                                _dtype_code(out), _stream(stream))
     _check(st, "tq_decode_split")
+    return out
+
+
+def attend_split(kcodec, vcodec, q, kpk, vpk, ctx, hkv, scale=0.0, out=None, scores_out=None,
+                 workspace=None, stream=None):
+    """Attention of q [batch, hq, n_q, 128] over split codes (SplitPacked with
+    rows [batch][hkv][ctx]); returns out [batch, hq, n_q, 128] fp32."""
+    _device_tensor(q, "q")
+    batch, hq, n_q, d = q.shape
+    if d != 128:
+        raise ValueError("split attention takes 128 channels")
+    if out is None:
+        out = torch.empty((batch, hq, n_q, d), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        need = attend_workspace_bytes(batch, n_q, hq, hkv, ctx, d)
+        workspace = torch.zeros((max(need, 1),), dtype=torch.uint8, device=q.device)
+    wbytes = workspace.numel() * workspace.element_size()
+    st = lib().tq_attend_split(ctypes.byref(kcodec.struct), ctypes.byref(vcodec.struct), _ptr(q),
+                               _dtype_code(q), batch, n_q, hq, hkv, kpk.structs, vpk.structs,
+                               int(ctx), float(scale), _ptr(out), _ptr(scores_out), _ptr(workspace),
+                               wbytes, _stream(stream))
+    _check(st, "tq_attend_split")
     return out
 
 

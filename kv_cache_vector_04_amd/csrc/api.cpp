@@ -250,6 +250,35 @@ extern "C" size_t tq_attend_decode_workspace(int batch, int n_q, int hq, int hkv
   return tqk::attend_workspace_bytes(batch, n_q, hq, hkv, ctx, d);
 }
 
+extern "C" int tq_attend_split(const tq_split_codec* kc, const tq_split_codec* vc, const void* q,
+                               int q_dtype, int batch, int n_q, int hq, int hkv, const tq_packed* k,
+                               const tq_packed* v, int64_t ctx, float scale, float* out,
+                               float* scores_out, void* workspace, size_t workspace_bytes,
+                               tq_stream_t stream) {
+  if (kc == nullptr || vc == nullptr) return TQ_ERR_INVALID_ARG;
+  int st = check_split(kc, k);
+  if (st != TQ_OK) return st;
+  if ((st = check_split(vc, v)) != TQ_OK) return st;
+  if (kc->hi.mode != TQ_PROD || kc->lo.mode != TQ_PROD || vc->hi.mode != TQ_MSE || vc->lo.mode != TQ_MSE)
+    return TQ_ERR_UNSUPPORTED;
+  if (!tqk::decode_split_supported(*kc, *vc)) return TQ_ERR_UNSUPPORTED;
+  if (q == nullptr || out == nullptr || !aligned(q, 16) || !aligned(out, 16)) return TQ_ERR_INVALID_ARG;
+  if (q_dtype != TQ_F16 && q_dtype != TQ_F32) return TQ_ERR_INVALID_ARG;
+  if (batch <= 0 || n_q <= 0 || hq <= 0 || hkv <= 0 || ctx <= 0) return TQ_ERR_INVALID_ARG;
+  if (hq % hkv) return TQ_ERR_INVALID_ARG;
+  if ((hq / hkv) * n_q > 16) return TQ_ERR_UNSUPPORTED;
+  if (ctx > ((int64_t)1 << 26)) return TQ_ERR_UNSUPPORTED;      // 32-bit offsets in a token range
+  if (!(scale >= 0.f)) return TQ_ERR_INVALID_ARG;
+  for (int h = 0; h < 2; ++h)
+    if (!aligned(k[h].qjl, 8) || !aligned(v[h].idx, 4)) return TQ_ERR_INVALID_ARG;
+  const size_t need = tqk::attend_workspace_bytes(batch, n_q, hq, hkv, ctx, 128);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16)))
+    return TQ_ERR_WORKSPACE;
+  return hip_status(tqk::launch_decode_split(*kc, *vc, q, q_dtype, batch, n_q, hq, hkv, k, v, ctx,
+                                             scale, out, scores_out, workspace,
+                                             reinterpret_cast<hipStream_t>(stream)));
+}
+
 extern "C" int tq_attend_decode(const tq_codec* kc, const tq_codec* vc, const void* q,
                                 int q_dtype, int batch, int n_q, int hq, int hkv,
                                 const tq_rope* q_rope, const tq_packed* k,

@@ -544,12 +544,13 @@ struct MergeParams {
   const float* part;
   float* out;
   int hq, hkv, n_q, G, nchunks, splits;
-  float inv_sqrt_d;
+  int wht_len;            // d, or 64 for the two halves of a split codec
+  float inv_sqrt_d;       // 1 / sqrt(wht_len)
   uint32_t vflip[48];
 };
 
 // Log-sum-exp merge of the token ranges of one query row, then
-// o = D_V * (H a) / sqrt(d).
+// o = D_V * (H a) / sqrt(d) (for a split codec H is H_64 on each half).
 template <int D>
 __global__ __launch_bounds__(D) void merge_kernel(MergeParams p) {
   constexpr int REC = D + 2;
@@ -601,8 +602,7 @@ __global__ __launch_bounds__(D) void merge_kernel(MergeParams p) {
     M = Mc;
   }
   v /= L;
-#pragma unroll
-  for (int hh = 1; hh < D; hh <<= 1) {
+  for (int hh = 1; hh < p.wht_len; hh <<= 1) {
     __syncthreads();
     s_v[i] = v;
     __syncthreads();
@@ -710,6 +710,7 @@ hipError_t launch_decode(const tq_codec& kc, const tq_codec& vc, const void* q, 
   mp.out = out;
   mp.hq = hq; mp.hkv = hkv; mp.n_q = n_q; mp.G = hq / hkv; mp.nchunks = nchunks;
   mp.splits = splits;
+  mp.wht_len = d;
   mp.inv_sqrt_d = p.inv_sqrt_d;
   for (int w = 0; w < 48; ++w) mp.vflip[w] = vc.flip[w];
   const unsigned rows = (unsigned)((int64_t)batch * hq * n_q);
@@ -717,6 +718,523 @@ hipError_t launch_decode(const tq_codec& kc, const tq_codec& vc, const void* q, 
     hipLaunchKernelGGL((merge_kernel<128>), dim3(rows), dim3(128), 0, stream, mp);
   else
     hipLaunchKernelGGL((merge_kernel<64>), dim3(rows), dim3(64), 0, stream, mp);
+  return hipGetLastError();
+}
+
+
+// ---------------------------------------------------------------------------
+// Attention from outlier-split codes.  Keys and values are each two d = 64
+// codecs over the channel halves [0, 64) (hi) and [64, 128) (lo), so with
+// q_h the query's half h:
+//   s_j = scale sum_h nu_hj ( <Pi_h q_h, c_Kh[idx_hj]> +
+//                             sqrt(pi/2)/64 gamma_hj <S_h Pi_h q_h, 2 sigma_hj - 1> )
+//   o_h = Pi_Vh^T sum_j softmax(s)_j nu^V_hj c_Vh[idx^V_hj]
+// The layout of decode_kernel, with: the query rotation stopped before the
+// butterfly stage across the halves (H_64 on each half, per-half flips,
+// 1/8); S block-diagonal; one key table per half at its own width; the QJL
+// byte table over the 16 bytes of the two halves (8 each) summed per half;
+// two weights per token (one per half's value norm); lanes 0..7 of each
+// 16-lane group accumulate hi coordinates, 8..15 lo ones, at their half's
+// code width.  The merge kernel applies H_64 per half.
+
+struct DecodeSplitParams {
+  const void* q;
+  int q_f16;
+  const uint8_t* kidx[2];
+  const uint8_t* kqjl[2];
+  const float* knorm[2];
+  const float* krnorm[2];
+  const uint8_t* vidx[2];
+  const float* vnorm[2];
+  const float* S[2];           // 64 x 64 row-major per half
+  float* scores_out;
+  float* part;
+  int64_t ctx;
+  int batch, hq, hkv, n_q, G, nchunks, splits;
+  int64_t split_len;
+  float scale;
+  float qjl_scale;             // sqrt(pi/2) / 64
+  float kcent[2][16];
+  float vcent[2][16];
+  uint32_t kflip[4];           // bit i: channel i (hi 0..63, lo 64..127)
+};
+
+template <int CBKH, int CBKL, int CBVH, int CBVL>
+struct SplitGeom {
+  using KH = KGroup<CBKH>;
+  using KL = KGroup<CBKL>;
+  static constexpr int D = 128, HD = 64;
+  static constexpr int NFH = HD / KH::gk, NFL = HD / KL::gk;
+  static constexpr int NEH = KH::entries, NEL = KL::entries;
+  static constexpr int WKH = HD * CBKH / 32, WKL = HD * CBKL / 32;
+  static constexpr int KROWH = HD * CBKH / 8, KROWL = HD * CBKL / 8;
+  static constexpr int NB = 16;                  // QJL bytes per token, 8 per half
+  static constexpr int VROWH = HD * CBVH / 8, VROWL = HD * CBVL / 8;
+  static constexpr int NVEH = 1 << (2 * CBVH), NVEL = 1 << (2 * CBVL);
+  static constexpr int CG = D / 8, TS = kWave / CG, TPL = kWave / TS;
+  // 8 waves (2 per SIMD): the two halves' tables, sums and weights need
+  // more than the 168 registers of 3 waves per SIMD
+  static constexpr int kWaves = 8, kThreads = kWaves * kWave;
+  static constexpr int LKH_B = NFH * NEH * 16, LKL_B = NFL * NEL * 16;
+  static constexpr int LQ_B = NB * 256 * 16;
+  static constexpr int MRG_B = kWaves * kDecRows * (D + 2) * 4;
+  static constexpr int TAB0_B = LKH_B + LKL_B + LQ_B;
+  static constexpr int TAB_B = TAB0_B > MRG_B ? TAB0_B : MRG_B;
+  static constexpr int KP = 4;                   // S column parts per half
+  static constexpr int W_B = kWaves * kWave * 2 * 16;
+  static constexpr int NIB_B = NB * 2 * 16 * 16;
+  static constexpr int SQP_B = KP * D * 16;
+  static constexpr int WN0_B = W_B > NIB_B ? W_B : NIB_B;
+  static constexpr int WN_B = WN0_B > SQP_B ? WN0_B : SQP_B;
+};
+
+template <int CBKH, int CBKL>
+struct SplitTile {
+  uint32_t kh[SplitGeom<CBKH, CBKL, 2, 2>::WKH];
+  uint32_t kl[SplitGeom<CBKH, CBKL, 2, 2>::WKL];
+  uint32_t sb[4];
+  float nkh, nkl, gh, gl, nvh, nvl;
+};
+
+constexpr int kSplitThreads = 8 * kWave;
+
+template <int CBKH, int CBKL, int CBVH, int CBVL>
+__global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeSplitParams p) {
+  using Gm = SplitGeom<CBKH, CBKL, CBVH, CBVL>;
+  static_assert(Gm::kThreads == kSplitThreads, "launch bounds");
+  using KH = typename Gm::KH;
+  using KL = typename Gm::KL;
+  constexpr int D = Gm::D, HD = Gm::HD, kW = Gm::kWaves, kT = Gm::kThreads;
+  constexpr int NFH = Gm::NFH, NFL = Gm::NFL, NEH = Gm::NEH, NEL = Gm::NEL, NB = Gm::NB;
+  constexpr int CG = Gm::CG, TS = Gm::TS, TPL = Gm::TPL;
+
+  __shared__ __align__(16) unsigned char s_tab[Gm::TAB_B];   // LK hi | LK lo | LQ
+  __shared__ __align__(16) float2 s_lv[Gm::NVEH + Gm::NVEL];
+  __shared__ __align__(16) unsigned char s_wn[Gm::WN_B];     // weights / set-up scratch
+  __shared__ __align__(16) float4 s_qT[D];
+  __shared__ __align__(16) float4 s_sT[D];
+  __shared__ float s_tot[2][kDecRows];
+  __shared__ float s_kc[2][16], s_vc[2][16];
+
+  float4* s_lkh = reinterpret_cast<float4*>(s_tab);
+  float4* s_lkl = reinterpret_cast<float4*>(s_tab + Gm::LKH_B);
+  float4* s_lq = reinterpret_cast<float4*>(s_tab + Gm::LKH_B + Gm::LKL_B);
+  float4* s_w = reinterpret_cast<float4*>(s_wn);               // [wave][lane][half]
+  float4* s_nib = reinterpret_cast<float4*>(s_wn);
+
+  const int tid = threadIdx.x;
+  // the wave index is uniform: scalar, so the token loop below is too
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int bgc = blockIdx.x;
+  const int split = blockIdx.y;
+  const int bg = bgc / p.nchunks, chunk = bgc % p.nchunks;
+  const int b = bg / p.hkv, g = bg % p.hkv;
+  const int qr_total = p.G * p.n_q;
+  const int lr0 = chunk * kDecRows;
+  const int nrows = (qr_total - lr0) < kDecRows ? (qr_total - lr0) : kDecRows;
+  const int64_t row_base = ((int64_t)b * p.hq + (int64_t)g * p.G) * p.n_q + lr0;
+  const int64_t t0 = (int64_t)split * p.split_len;
+  int64_t t1 = t0 + p.split_len;
+  if (t1 > p.ctx) t1 = p.ctx;
+  const int64_t kv_base = (int64_t)bg * p.ctx;
+  // value lanes: 8-coordinate group cg of the row, half vh, its code width
+  const int cg = lane % CG, ts = lane / CG;
+  const int vh = cg >> 3, cgl = cg & 7;
+  const int cbv = vh ? CBVL : CBVH;
+  const int vbit0 = cgl * 8 * cbv;
+  const int vw0 = vbit0 >> 5;
+  const int vwords = 2 * cbv;
+  const int vw1 = (vw0 + 1) < vwords ? (vw0 + 1) : (vwords - 1);
+  const bool vstraddle = (vbit0 & 31) + 8 * cbv > 32;
+  const uint32_t vrow = vh ? Gm::VROWL : Gm::VROWH;
+  // the lane's value plane from this range's first token: one 64-bit base,
+  // then 32-bit offsets (a range is under 2^26 tokens of at most 32 bytes)
+  const uint32_t* vbase =
+      reinterpret_cast<const uint32_t*>((vh ? p.vidx[1] : p.vidx[0]) + (kv_base + t0) * vrow) + vw0;
+  const int lvoff = vh ? Gm::NVEH : 0;
+  const uint32_t vmask = (1u << (2 * cbv)) - 1u;
+
+  // the ten planes of the key side from this range's first token (uniform
+  // bases), addressed with one 32-bit token offset per lane
+  const int64_t rb = kv_base + t0;
+  const uint8_t* const kih = p.kidx[0] + rb * Gm::KROWH;
+  const uint8_t* const kil = p.kidx[1] + rb * Gm::KROWL;
+  const uint2* const kqh = reinterpret_cast<const uint2*>(p.kqjl[0] + rb * 8);
+  const uint2* const kql = reinterpret_cast<const uint2*>(p.kqjl[1] + rb * 8);
+  const float* const nkh = p.knorm[0] + rb;
+  const float* const nkl = p.knorm[1] + rb;
+  const float* const gkh = p.krnorm[0] + rb;
+  const float* const gkl = p.krnorm[1] + rb;
+  const float* const nvh = p.vnorm[0] + rb;
+  const float* const nvl = p.vnorm[1] + rb;
+  auto load_tile = [&](int64_t tile, SplitTile<CBKH, CBKL>& R) {
+    const int64_t tok = tile + lane;
+    const uint32_t rel = tok < t1 ? (uint32_t)(tok - t0) : 0u;
+    load_words<Gm::WKH, (Gm::KROWH % 16 == 0) ? 16 : 8>(kih + rel * Gm::KROWH, R.kh);
+    load_words<Gm::WKL, (Gm::KROWL % 16 == 0) ? 16 : 8>(kil + rel * Gm::KROWL, R.kl);
+    const uint2 sh = kqh[rel];
+    const uint2 sl = kql[rel];
+    R.sb[0] = sh.x; R.sb[1] = sh.y; R.sb[2] = sl.x; R.sb[3] = sl.y;
+    R.nkh = nkh[rel] * p.scale;
+    R.nkl = nkl[rel] * p.scale;
+    R.gh = gkh[rel] * p.qjl_scale;
+    R.gl = gkl[rel] * p.qjl_scale;
+    R.nvh = nvh[rel];
+    R.nvl = nvl[rel];
+  };
+
+  SplitTile<CBKH, CBKL> cur;
+  const int64_t first = t0 + (int64_t)wave * kWave;
+  if (first < t1) load_tile(first, cur);
+
+  // ---- set-up ----
+  // S rows for Sq: thread -> (row si, column part spart of si's half)
+  constexpr int KP = Gm::KP, KLN = HD / KP;
+  const int si = tid % D, spart = tid / D;
+  const bool sq_thread = spart < KP;
+  const int sh_half = si / HD;
+  float4 srow[KLN / 4];
+  if (sq_thread) {
+    const float4* S4 = reinterpret_cast<const float4*>(p.S[sh_half] + (size_t)(si % HD) * HD + spart * KLN);
+#pragma unroll
+    for (int j = 0; j < KLN / 4; ++j) srow[j] = S4[j];
+  }
+  const DecodeSplitParams* kp = (const DecodeSplitParams*)__builtin_amdgcn_kernarg_segment_ptr();
+  if (tid < 32) {
+    s_kc[tid >> 4][tid & 15] = kp->kcent[tid >> 4][tid & 15];
+    s_vc[tid >> 4][tid & 15] = kp->vcent[tid >> 4][tid & 15];
+  }
+  // q_h -> H_64 (D_h q_h) / 8: wave r < 4 rotates query row r, lane l holding
+  // channels 2 l, 2 l + 1 (lanes 0..31 the hi half); the lane-exchange
+  // stages stop below 32, the stage that would mix the halves
+  if (wave < kDecRows) {
+    const int r = wave;
+    float x[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int i = 2 * lane + c;
+      float v = 0.f;
+      if (r < nrows) {
+        const int64_t off = (row_base + r) * D + i;
+        v = p.q_f16 ? (float)reinterpret_cast<const _Float16*>(p.q)[off]
+                    : reinterpret_cast<const float*>(p.q)[off];
+      }
+      x[c] = ((kp->kflip[i >> 5] >> (i & 31)) & 1u) ? -v : v;
+    }
+    {
+      const float a = x[0], bb = x[1];
+      x[0] = a + bb;
+      x[1] = a - bb;
+    }
+#pragma unroll
+    for (int lb = 1; lb < kWave / 2; lb <<= 1) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const float o = __shfl_xor(x[c], lb);
+        x[c] = (lane & lb) ? (o - x[c]) : (x[c] + o);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) reinterpret_cast<float*>(s_qT)[4 * (2 * lane + c) + r] = x[c] * 0.125f;
+  }
+  __syncthreads();                                  // q_rot and the centroids
+  float4* s_sqp = reinterpret_cast<float4*>(s_wn);
+  if (sq_thread) {
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < KLN / 4; ++j) {
+      const int k = sh_half * HD + spart * KLN + 4 * j;
+      a = f4fma(s_qT[k], srow[j].x, a);
+      a = f4fma(s_qT[k + 1], srow[j].y, a);
+      a = f4fma(s_qT[k + 2], srow[j].z, a);
+      a = f4fma(s_qT[k + 3], srow[j].w, a);
+    }
+    s_sqp[spart * D + si] = a;
+  }
+  for (int t = tid; t < NFH * NEH; t += kT) {
+    const int v = t % NEH, f = t / NEH;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int e = 0; e < KH::gk; ++e)
+      a = f4fma(s_qT[f * KH::gk + e], s_kc[0][(v >> (e * CBKH)) & ((1 << CBKH) - 1)], a);
+    s_lkh[t] = a;
+  }
+  for (int t = tid; t < NFL * NEL; t += kT) {
+    const int v = t % NEL, f = t / NEL;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int e = 0; e < KL::gk; ++e)
+      a = f4fma(s_qT[HD + f * KL::gk + e], s_kc[1][(v >> (e * CBKL)) & ((1 << CBKL) - 1)], a);
+    s_lkl[t] = a;
+  }
+  for (int t = tid; t < Gm::NVEH; t += kT)
+    s_lv[t] = make_float2(s_vc[0][t & ((1 << CBVH) - 1)], s_vc[0][t >> CBVH]);
+  for (int t = tid; t < Gm::NVEL; t += kT)
+    s_lv[Gm::NVEH + t] = make_float2(s_vc[1][t & ((1 << CBVL) - 1)], s_vc[1][t >> CBVL]);
+  __syncthreads();                                  // Sq partials, LK, LV
+  if (tid < D) {
+    float4 a = s_sqp[tid];
+#pragma unroll
+    for (int q = 1; q < KP; ++q) a = f4add(a, s_sqp[q * D + tid]);
+    s_sT[tid] = a;
+  }
+  __syncthreads();                                  // Sq
+  // tot[h][r] = sum over half h of Sq[r][i]: wave r, one half after the other
+  if (wave < kDecRows) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float t = wave_sum(reinterpret_cast<const float*>(s_sT)[4 * (h * HD + lane) + wave]);
+      if (lane == 0) s_tot[h][wave] = t;
+    }
+  }
+  for (int t = tid; t < NB * 32; t += kT) {
+    const int pb = t >> 5, h = (t >> 4) & 1, n = t & 15;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if ((n >> e) & 1) a = f4add(a, s_sT[8 * pb + 4 * h + e]);
+    s_nib[t] = a;
+  }
+  __syncthreads();                                  // nibble sums, tot
+  for (int t = tid; t < NB * 256; t += kT) {
+    const int pb = t >> 8, v = t & 255;
+    s_lq[t] = f4add(s_nib[pb * 32 + (v & 15)], s_nib[pb * 32 + 16 + (v >> 4)]);
+  }
+  __syncthreads();
+  const float4 toth = make_float4(s_tot[0][0], s_tot[0][1], s_tot[0][2], s_tot[0][3]);
+  const float4 totl = make_float4(s_tot[1][0], s_tot[1][1], s_tot[1][2], s_tot[1][3]);
+
+  // ---- scan ----
+  float m_run[kDecRows], l_run[kDecRows];
+  float acc[kDecRows][8];
+#pragma unroll
+  for (int r = 0; r < kDecRows; ++r) {
+    m_run[r] = -INFINITY;
+    l_run[r] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[r][e] = 0.f;
+  }
+  const float4* __restrict__ lkh = s_lkh;
+  const float4* __restrict__ lkl = s_lkl;
+  const float4* __restrict__ lq = s_lq;
+
+  for (int64_t tile = first; tile < t1; tile += (int64_t)kW * kWave) {
+    const SplitTile<CBKH, CBKL> R = cur;
+    const int64_t next = tile + (int64_t)kW * kWave;
+    if (next < t1) load_tile(next, cur);
+    const int64_t tok = tile + lane;
+    const bool valid = tok < t1;
+    float4 mh[2] = {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
+    float4 ml[2] = {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
+#pragma unroll
+    for (int f = 0; f < NFH; ++f) {
+      const uint32_t v = field_bits<Gm::WKH>(R.kh, f * KH::bits, KH::bits);
+      mh[f & 1] = f4add(mh[f & 1], lkh[f * NEH + v]);
+      // bound the table reads in flight (each holds 4 registers)
+      if ((f & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int f = 0; f < NFL; ++f) {
+      const uint32_t v = field_bits<Gm::WKL>(R.kl, f * KL::bits, KL::bits);
+      ml[f & 1] = f4add(ml[f & 1], lkl[f * NEL + v]);
+      if ((f & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    float4 qh = make_float4(0.f, 0.f, 0.f, 0.f), ql = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int pb = 0; pb < NB; ++pb) {
+      const uint32_t v = (R.sb[pb >> 2] >> (8 * (pb & 3))) & 255u;
+      if (pb < NB / 2) qh = f4add(qh, lq[pb * 256 + v]);
+      else ql = f4add(ql, lq[pb * 256 + v]);
+      if ((pb & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+    }
+    const float4 msh = f4add(mh[0], mh[1]), msl = f4add(ml[0], ml[1]);
+    float s[kDecRows];
+    s[0] = R.nkh * fmaf(R.gh, 2.f * qh.x - toth.x, msh.x) + R.nkl * fmaf(R.gl, 2.f * ql.x - totl.x, msl.x);
+    s[1] = R.nkh * fmaf(R.gh, 2.f * qh.y - toth.y, msh.y) + R.nkl * fmaf(R.gl, 2.f * ql.y - totl.y, msl.y);
+    s[2] = R.nkh * fmaf(R.gh, 2.f * qh.z - toth.z, msh.z) + R.nkl * fmaf(R.gl, 2.f * ql.z - totl.z, msl.z);
+    s[3] = R.nkh * fmaf(R.gh, 2.f * qh.w - toth.w, msh.w) + R.nkl * fmaf(R.gl, 2.f * ql.w - totl.w, msl.w);
+    if (p.scores_out != nullptr && valid) {
+#pragma unroll
+      for (int r = 0; r < kDecRows; ++r)
+        if (r < nrows) p.scores_out[(row_base + r) * p.ctx + tok] = s[r];
+    }
+    // this tile's value codes, four tokens at a time: the next four load
+    // while the current four accumulate (the split's two widths leave no
+    // room to hold all sixteen through the scores)
+    constexpr int VC = 4;
+    const uint32_t trel = (uint32_t)(tile - t0) + (uint32_t)ts, tlast = (uint32_t)(t1 - 1 - t0);
+    auto load_v = [&](int u0, uint32_t (&dst)[VC][2]) {
+#pragma unroll
+      for (int q = 0; q < VC; ++q) {
+        uint32_t vt = trel + (uint32_t)((u0 + q) * TS);
+        vt = vt <= tlast ? vt : 0u;
+        const uint32_t* vr = vbase + vt * (vrow >> 2);
+        dst[q][0] = vr[0];
+        dst[q][1] = vstraddle ? vr[vw1 - vw0] : 0u;
+      }
+    };
+    uint32_t vnext[VC][2];
+    load_v(0, vnext);
+    float pe[kDecRows];
+#pragma unroll
+    for (int r = 0; r < kDecRows; ++r) {
+      const float sv = valid ? s[r] : -INFINITY;
+      const float mt = wave_max(sv);
+      const float mn = fmaxf(m_run[r], mt);
+      const float alpha = __expf(m_run[r] - mn);
+      m_run[r] = mn;
+      const float e = valid ? __expf(sv - mn) : 0.f;
+      l_run[r] = fmaf(l_run[r], alpha, e);
+      pe[r] = e;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[r][k] *= alpha;
+    }
+    s_w[(wave * kWave + lane) * 2] =
+        make_float4(pe[0] * R.nvh, pe[1] * R.nvh, pe[2] * R.nvh, pe[3] * R.nvh);
+    s_w[(wave * kWave + lane) * 2 + 1] =
+        make_float4(pe[0] * R.nvl, pe[1] * R.nvl, pe[2] * R.nvl, pe[3] * R.nvl);
+    // LDS operations of one wave complete in order: no workgroup barrier
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int u = 0; u < TPL; ++u) {
+      uint32_t vcur[2] = {vnext[u % VC][0], vnext[u % VC][1]};
+      if (u % VC == VC - 1 && u + 1 < TPL) load_v(u + 1, vnext);
+      const float4 w = s_w[(wave * kWave + u * TS + ts) * 2 + vh];
+      const uint32_t bits = vstraddle ? __builtin_amdgcn_alignbit(vcur[1], vcur[0], vbit0 & 31)
+                                      : (vcur[0] >> (vbit0 & 31));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t pv = (bits >> (2 * cbv * e)) & vmask;
+        const float2 c2 = s_lv[lvoff + pv];
+        acc[0][2 * e] = fmaf(w.x, c2.x, acc[0][2 * e]);
+        acc[0][2 * e + 1] = fmaf(w.x, c2.y, acc[0][2 * e + 1]);
+        acc[1][2 * e] = fmaf(w.y, c2.x, acc[1][2 * e]);
+        acc[1][2 * e + 1] = fmaf(w.y, c2.y, acc[1][2 * e + 1]);
+        acc[2][2 * e] = fmaf(w.z, c2.x, acc[2][2 * e]);
+        acc[2][2 * e + 1] = fmaf(w.z, c2.y, acc[2][2 * e + 1]);
+        acc[3][2 * e] = fmaf(w.w, c2.x, acc[3][2 * e]);
+        acc[3][2 * e + 1] = fmaf(w.w, c2.y, acc[3][2 * e + 1]);
+      }
+      if ((u & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // ---- merge the waves, write this range's (acc, max, sum) per row ----
+#pragma unroll
+  for (int r = 0; r < kDecRows; ++r) {
+    l_run[r] = wave_sum(l_run[r]);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+#pragma unroll
+      for (int off = CG; off < kWave; off <<= 1) acc[r][k] += __shfl_xor(acc[r][k], off);
+    }
+  }
+  __syncthreads();
+  constexpr int REC = D + 2;
+  float* mrg = reinterpret_cast<float*>(s_tab);
+  if (ts == 0) {
+#pragma unroll
+    for (int r = 0; r < kDecRows; ++r)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) mrg[(wave * kDecRows + r) * REC + 8 * cg + k] = acc[r][k];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < kDecRows; ++r) {
+      mrg[(wave * kDecRows + r) * REC + D] = m_run[r];
+      mrg[(wave * kDecRows + r) * REC + D + 1] = l_run[r];
+    }
+  }
+  __syncthreads();
+  const int64_t rec0 = ((int64_t)bgc * p.splits + split) * kDecRows;
+  for (int t = tid; t < kDecRows * D; t += kT) {
+    const int r = t / D, i = t % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kW; ++w) M = fmaxf(M, mrg[(w * kDecRows + r) * REC + D]);
+    float a = 0.f, L = 0.f;
+#pragma unroll
+    for (int w = 0; w < kW; ++w) {
+      const float mw = mrg[(w * kDecRows + r) * REC + D];
+      const float f = mw == -INFINITY ? 0.f : __expf(mw - M);
+      a = fmaf(mrg[(w * kDecRows + r) * REC + i], f, a);
+      L = fmaf(mrg[(w * kDecRows + r) * REC + D + 1], f, L);
+    }
+    float* rec = p.part + (rec0 + r) * REC;
+    rec[i] = a;
+    if (i == 0) {
+      rec[D] = M;
+      rec[D + 1] = L;
+    }
+  }
+}
+
+template <int CBKH, int CBKL, int CBVH, int CBVL>
+static hipError_t run_decode_split(const DecodeSplitParams& p, dim3 grid, hipStream_t s) {
+  hipLaunchKernelGGL((decode_split_kernel<CBKH, CBKL, CBVH, CBVL>), grid,
+                     dim3(SplitGeom<CBKH, CBKL, CBVH, CBVL>::kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+bool decode_split_supported(const tq_split_codec& kc, const tq_split_codec& vc) {
+  const int kh = kc.hi.code_bits, kl = kc.lo.code_bits, vh = vc.hi.code_bits, vl = vc.lo.code_bits;
+  const bool kok = (kh == 2 && kl == 1) || (kh == 3 && kl == 2);
+  const bool vok = (vh == 3 && vl == 2) || (vh == 4 && vl == 3);
+  return kok && vok;
+}
+
+hipError_t launch_decode_split(const tq_split_codec& kc, const tq_split_codec& vc, const void* q,
+                               int q_dtype, int batch, int n_q, int hq, int hkv, const tq_packed* k,
+                               const tq_packed* v, int64_t ctx, float scale, float* out,
+                               float* scores_out, void* workspace, hipStream_t stream) {
+  int nchunks, splits;
+  int64_t split_len;
+  plan_decode(batch, n_q, hq, hkv, ctx, nchunks, splits, split_len);
+  const size_t groups = (size_t)batch * hkv * nchunks;
+  DecodeSplitParams p = {};
+  p.q = q;
+  p.q_f16 = q_dtype == TQ_F16;
+  for (int h = 0; h < 2; ++h) {
+    const tq_codec& kh = h ? kc.lo : kc.hi;
+    const tq_codec& vh = h ? vc.lo : vc.hi;
+    p.kidx[h] = k[h].idx; p.kqjl[h] = k[h].qjl; p.knorm[h] = k[h].norm; p.krnorm[h] = k[h].rnorm;
+    p.vidx[h] = v[h].idx; p.vnorm[h] = v[h].norm;
+    p.S[h] = kh.S;
+    for (int i = 0; i < 16; ++i) { p.kcent[h][i] = kh.centroids[i]; p.vcent[h][i] = vh.centroids[i]; }
+    p.kflip[2 * h] = kh.flip[0];
+    p.kflip[2 * h + 1] = kh.flip[1];
+  }
+  p.scores_out = scores_out;
+  p.part = reinterpret_cast<float*>(workspace);
+  p.ctx = ctx; p.batch = batch; p.hq = hq; p.hkv = hkv; p.n_q = n_q; p.G = hq / hkv;
+  p.nchunks = nchunks; p.splits = splits; p.split_len = split_len;
+  p.scale = scale > 0.f ? scale : (float)(1.0 / std::sqrt(128.0));
+  p.qjl_scale = (float)(std::sqrt(M_PI / 2.0) / 64.0);
+  const dim3 grid((unsigned)groups, (unsigned)splits);
+  const int key = kc.hi.code_bits * 1000 + kc.lo.code_bits * 100 + vc.hi.code_bits * 10 + vc.lo.code_bits;
+  hipError_t e;
+  switch (key) {
+    case 2132: e = run_decode_split<2, 1, 3, 2>(p, grid, stream); break;
+    case 2143: e = run_decode_split<2, 1, 4, 3>(p, grid, stream); break;
+    case 3232: e = run_decode_split<3, 2, 3, 2>(p, grid, stream); break;
+    case 3243: e = run_decode_split<3, 2, 4, 3>(p, grid, stream); break;
+    default: return hipErrorNotSupported;
+  }
+  if (e != hipSuccess) return e;
+  MergeParams mp = {};
+  mp.part = p.part;
+  mp.out = out;
+  mp.hq = hq; mp.hkv = hkv; mp.n_q = n_q; mp.G = hq / hkv; mp.nchunks = nchunks;
+  mp.splits = splits;
+  mp.wht_len = 64;
+  mp.inv_sqrt_d = 0.125f;
+  mp.vflip[0] = vc.hi.flip[0]; mp.vflip[1] = vc.hi.flip[1];
+  mp.vflip[2] = vc.lo.flip[0]; mp.vflip[3] = vc.lo.flip[1];
+  const unsigned rows = (unsigned)((int64_t)batch * hq * n_q);
+  hipLaunchKernelGGL((merge_kernel<128>), dim3(rows), dim3(128), 0, stream, mp);
   return hipGetLastError();
 }
 

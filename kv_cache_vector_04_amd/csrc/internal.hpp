@@ -42,6 +42,16 @@ hipError_t launch_decode_vq(const tq_vq_codec& c, const uint8_t* idx, const floa
 hipError_t launch_materialize(const tq_codec& c, const tq_packed& in, int64_t n_rows, void* out,
                               int out_dtype, hipStream_t stream, int64_t out_stride = 0);
 
+// Attention from outlier-split codes (decode.hip): keys prod and values mse,
+// each two d = 64 halves; table widths (hi, lo) of (2, 1) or (3, 2) for keys
+// and (3, 2) or (4, 3) for values; G n_q <= 16; the workspace of the d = 128
+// decode path.
+bool decode_split_supported(const tq_split_codec& kc, const tq_split_codec& vc);
+hipError_t launch_decode_split(const tq_split_codec& kc, const tq_split_codec& vc, const void* q,
+                               int q_dtype, int batch, int n_q, int hq, int hkv, const tq_packed* k,
+                               const tq_packed* v, int64_t ctx, float scale, float* out,
+                               float* scores_out, void* workspace, hipStream_t stream);
+
 // d = 1536 (wide.hip).  The encode workspace holds S as fp16 hi / lo planes
 // and the residual planes of one block of vectors (prod only); the scan
 // workspace holds the S planes and the four query planes.

@@ -149,6 +149,61 @@ def test_split_attention_through_the_decoder():
     assert row_rel_err(o, want).max() <= 1e-3
 
 
+def oracle_split_codes(kp, vp, ks, vs, rows):
+    gk = tuple(as_encoded({k: v[rows] for k, v in gpu_codes(pk, 64, c.code_bits, c.m).items()})
+               for pk, c in ((kp.hi, ks.hi), (kp.lo, ks.lo)))
+    gv = tuple(as_encoded({k: v[rows] for k, v in gpu_codes(pk, 64, c.code_bits).items()})
+               for pk, c in ((vp.hi, vs.hi), (vp.lo, vs.lo)))
+    return gk, gv
+
+
+@pytest.mark.parametrize("b_hi,b_lo", [(3, 2), (4, 3)])
+@pytest.mark.parametrize("G,n_q", [(4, 1), (2, 3)])
+def test_split_attention_from_codes(b_hi, b_lo, G, n_q):
+    """tq_attend_split against the oracle's attention over the GPU's own split
+    codes, per (batch, query head, query): outputs and scores within 1e-3 per
+    row; ragged context, two batches, two KV heads, fp16 queries."""
+    say("attend split %d/%d G=%d n_q=%d" % (b_hi, b_lo, G, n_q))
+    rng = np.random.default_rng(600 + 10 * b_hi + G + n_q)
+    batch, hkv, ctx = 2, 2, 3000 + 37
+    hq = hkv * G
+    n = batch * hkv * ctx
+    k = rng.standard_t(3, (n, 128)) * rng.uniform(0.2, 3, (n, 1))
+    k[:, [0, 9, 21, 50]] *= 8.0
+    v = rng.standard_normal((n, 128))
+    q = rng.standard_normal((batch, hq, n_q, 128)).astype(np.float16)
+    ks, vs, ko, vo = make(rng, b_hi, b_lo)
+    kp, vp = tq.encode_split(ks, vs, torch.from_numpy(k.astype(np.float16)).cuda(),
+                             torch.from_numpy(v.astype(np.float16)).cuda())
+    scores = torch.empty((batch, hq, n_q, ctx), dtype=torch.float32, device="cuda")
+    out = tq.attend_split(ks, vs, torch.from_numpy(q).cuda(), kp, vp, ctx, hkv, scores_out=scores)
+    torch.cuda.synchronize()
+    out, scores = to_np(out).astype(np.float64), to_np(scores).astype(np.float64)
+    for b in range(batch):
+        for g in range(hkv):
+            rows = np.arange((b * hkv + g) * ctx, (b * hkv + g + 1) * ctx)
+            gk, gv = oracle_split_codes(kp, vp, ks, vs, rows)
+            qq = q[b, g * G:(g + 1) * G].reshape(G * n_q, 128).astype(np.float64)
+            want = SP.attention_split(qq, gk, gv, 64, ko[0], ko[1], vo[0], vo[1])
+            got = out[b, g * G:(g + 1) * G].reshape(G * n_q, 128)
+            check_rows(got, want, tol=1e-3)
+            s_want = SP.estimate_split(qq, gk, 64, ko[0], ko[1]) / np.sqrt(128.0)
+            check_rows(scores[b, g * G:(g + 1) * G].reshape(G * n_q, ctx), s_want, tol=1e-3)
+
+
+def test_split_attention_validation():
+    rng = np.random.default_rng(3)
+    ks, vs, _, _ = make(rng, 3, 2)
+    kp, vp = tq.encode_split(ks, vs, torch.zeros((64, 128), dtype=torch.float16, device="cuda"),
+                             torch.zeros((64, 128), dtype=torch.float16, device="cuda"))
+    q = torch.zeros((1, 32, 1, 128), dtype=torch.float16, device="cuda")
+    with pytest.raises(tq.TQError):         # 32 query rows per KV head
+        tq.attend_split(ks, vs, q, kp, vp, 64, 1)
+    odd = tq.SplitCodec(*half_codec(rng, 4, True)[:1], *half_codec(rng, 2, True)[:1])
+    with pytest.raises(tq.TQError):         # table widths (3, 1): no kernel
+        tq.attend_split(odd, vs, q[:, :4], kp, vp, 64, 1)
+
+
 def test_split_full_size_gqa_sampled():
     """The GQA decode workload's K and V (8 x 32768 x 128, fp16 Student-t, four
     outlier channels x20 per head), each head's channels ordered by the
