@@ -1097,27 +1097,34 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeSplit
         make_float4(pe[0] * R.nvl, pe[1] * R.nvl, pe[2] * R.nvl, pe[3] * R.nvl);
     // LDS operations of one wave complete in order: no workgroup barrier
     __builtin_amdgcn_wave_barrier();
+    // chunks of VC tokens, not unrolled: an unrolled loop over all sixteen
+    // tokens spills (the table reads of every token get hoisted)
+#pragma unroll 1
+    for (int c = 0; c < TPL / VC; ++c) {
+      uint32_t vc4[VC][2];
 #pragma unroll
-    for (int u = 0; u < TPL; ++u) {
-      uint32_t vcur[2] = {vnext[u % VC][0], vnext[u % VC][1]};
-      if (u % VC == VC - 1 && u + 1 < TPL) load_v(u + 1, vnext);
-      const float4 w = s_w[(wave * kWave + u * TS + ts) * 2 + vh];
-      const uint32_t bits = vstraddle ? __builtin_amdgcn_alignbit(vcur[1], vcur[0], vbit0 & 31)
-                                      : (vcur[0] >> (vbit0 & 31));
+      for (int q = 0; q < VC; ++q) { vc4[q][0] = vnext[q][0]; vc4[q][1] = vnext[q][1]; }
+      if (c + 1 < TPL / VC) load_v((c + 1) * VC, vnext);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t pv = (bits >> (2 * cbv * e)) & vmask;
-        const float2 c2 = s_lv[lvoff + pv];
-        acc[0][2 * e] = fmaf(w.x, c2.x, acc[0][2 * e]);
-        acc[0][2 * e + 1] = fmaf(w.x, c2.y, acc[0][2 * e + 1]);
-        acc[1][2 * e] = fmaf(w.y, c2.x, acc[1][2 * e]);
-        acc[1][2 * e + 1] = fmaf(w.y, c2.y, acc[1][2 * e + 1]);
-        acc[2][2 * e] = fmaf(w.z, c2.x, acc[2][2 * e]);
-        acc[2][2 * e + 1] = fmaf(w.z, c2.y, acc[2][2 * e + 1]);
-        acc[3][2 * e] = fmaf(w.w, c2.x, acc[3][2 * e]);
-        acc[3][2 * e + 1] = fmaf(w.w, c2.y, acc[3][2 * e + 1]);
+      for (int q = 0; q < VC; ++q) {
+        const int u = c * VC + q;
+        const float4 w = s_w[(wave * kWave + u * TS + ts) * 2 + vh];
+        const uint32_t bits = vstraddle ? __builtin_amdgcn_alignbit(vc4[q][1], vc4[q][0], vbit0 & 31)
+                                        : (vc4[q][0] >> (vbit0 & 31));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t pv = (bits >> (2 * cbv * e)) & vmask;
+          const float2 c2 = s_lv[lvoff + pv];
+          acc[0][2 * e] = fmaf(w.x, c2.x, acc[0][2 * e]);
+          acc[0][2 * e + 1] = fmaf(w.x, c2.y, acc[0][2 * e + 1]);
+          acc[1][2 * e] = fmaf(w.y, c2.x, acc[1][2 * e]);
+          acc[1][2 * e + 1] = fmaf(w.y, c2.y, acc[1][2 * e + 1]);
+          acc[2][2 * e] = fmaf(w.z, c2.x, acc[2][2 * e]);
+          acc[2][2 * e + 1] = fmaf(w.z, c2.y, acc[2][2 * e + 1]);
+          acc[3][2 * e] = fmaf(w.w, c2.x, acc[3][2 * e]);
+          acc[3][2 * e + 1] = fmaf(w.w, c2.y, acc[3][2 * e + 1]);
+        }
       }
-      if ((u & 3) == 3) __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_wave_barrier();
   }

@@ -236,6 +236,34 @@ def test_vq_search_table_lists_every_nearest_codeword(L, d, n):
     assert np.all(full | member[cell, near])
 
 
+def test_attend_split_validation_before_launch(L):
+    def sc(mode, bh, bl):
+        return tq.TQSplitCodec(_codec_struct(L, 64, mode, bh), _codec_struct(L, 64, mode, bl))
+    kc, vc = sc(tq.TQ_PROD, 3, 2), sc(tq.TQ_MSE, 3, 2)
+    fake = ctypes.c_void_p(1 << 20)
+    kp = (tq.TQPacked * 2)(tq.TQPacked(1 << 20, 1 << 20, 1 << 20, 1 << 20),
+                           tq.TQPacked(1 << 20, 1 << 20, 1 << 20, 1 << 20))
+    vp = (tq.TQPacked * 2)(tq.TQPacked(1 << 20, None, 1 << 20, None), tq.TQPacked(1 << 20, None, 1 << 20, None))
+    att = L.tq_attend_split
+    K, V = ctypes.byref(kc), ctypes.byref(vc)
+    need = L.tq_attend_decode_workspace(1, 1, 32, 8, 4096, 128)
+
+    def call(k=K, v=V, q=fake, qd=tq.TQ_F16, b=1, nq=1, hq=32, hkv=8, ctx=4096, scale=0.0, ws=fake,
+             wsb=need):
+        return att(k, v, q, qd, b, nq, hq, hkv, kp, vp, ctx, scale, fake, None, ws, wsb, None)
+    assert call(k=None) == tq.TQ_ERR_INVALID_ARG
+    assert call(qd=5) == tq.TQ_ERR_INVALID_ARG
+    assert call(q=ctypes.c_void_p((1 << 20) + 4)) == tq.TQ_ERR_INVALID_ARG
+    assert call(hq=30) == tq.TQ_ERR_INVALID_ARG
+    assert call(ctx=0) == tq.TQ_ERR_INVALID_ARG
+    assert call(scale=-1.0) == tq.TQ_ERR_INVALID_ARG
+    assert call(hq=64, hkv=2) == tq.TQ_ERR_UNSUPPORTED          # 32 query rows per KV head
+    assert call(k=ctypes.byref(sc(tq.TQ_PROD, 4, 2))) == tq.TQ_ERR_UNSUPPORTED   # widths (3, 1)
+    assert call(k=V, v=K) == tq.TQ_ERR_INVALID_ARG              # mse keys lack QJL planes
+    assert call(ws=None) == tq.TQ_ERR_WORKSPACE
+    assert call(wsb=need - 16) == tq.TQ_ERR_WORKSPACE
+
+
 def test_wide_encode_workspace(L):
     kw = _codec_struct(L, 1536, tq.TQ_PROD, 2)
     fake = ctypes.c_void_p(1 << 20)
