@@ -189,6 +189,10 @@ __global__ __launch_bounds__(DecWaves<CBV>::kThreads) void decode_kernel(DecodeP
   // (where LDS allows: the 64 KB key table of 1- and 3-bit keys at d = 128
   // leaves no room, and those variants keep the two-word registers)
   constexpr bool VST = CBV == 3 && (D == 64 || CBK % 2 == 0);
+  // the other 3-bit variants load their value words after the scores, four
+  // tokens at a time (all sixteen tokens' two words through the scores
+  // spill at this register budget)
+  constexpr bool VCHUNK = CBV == 3 && !VST;
   constexpr int VSTR = VW + 1;
   __shared__ uint32_t s_vst[VST ? kDecWaves * kWave * VSTR : 1];
 
@@ -395,12 +399,12 @@ __global__ __launch_bounds__(DecWaves<CBV>::kThreads) void decode_kernel(DecodeP
     const int64_t tok = tile + lane;
     const bool valid = tok < t1;
     // this tile's value codes (used after the scores)
-    uint32_t vwr[TPL][2];
+    uint32_t vwr[VCHUNK ? 1 : TPL][2];
     uint32_t vrow[VST ? VW : 1];   // 3-bit codes: the lane's own token row, staged to LDS
     if constexpr (VST) {
       const int64_t vt = valid ? tok : t0;
       load_words<VW, (VROW % 16 == 0) ? 16 : 8>(p.vidx + (kv_base + vt) * VROW, vrow);
-    } else {
+    } else if constexpr (!VCHUNK) {
 #pragma unroll
       for (int u = 0; u < TPL; ++u) {
         int64_t vt = tile + (int64_t)u * TS + ts;
@@ -461,17 +465,9 @@ __global__ __launch_bounds__(DecWaves<CBV>::kThreads) void decode_kernel(DecodeP
     // LDS operations of one wave complete in order: the weights (and rows)
     // written above are visible to the reads below without a workgroup barrier.
     __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int u = 0; u < TPL; ++u) {
+    // weight of token u times the pair table entries of its four code pairs
+    auto accum = [&](int u, uint32_t bits) {
       const float4 w = s_w[wave * kWave + u * TS + ts];
-      uint32_t bits;
-      if constexpr (VST) {
-        const uint32_t* vr = s_vst + (wave * kWave + u * TS + ts) * VSTR;
-        bits = __builtin_amdgcn_alignbit(vr[vw1], vr[vw0], vbit0 & 31);
-      } else {
-        bits = vstraddle ? __builtin_amdgcn_alignbit(vwr[u][1], vwr[u][0], vbit0 & 31)
-                         : (vwr[u][0] >> (vbit0 & 31));
-      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint32_t pv = (bits >> (2 * CBV * e)) & (NVE - 1);
@@ -485,7 +481,49 @@ __global__ __launch_bounds__(DecWaves<CBV>::kThreads) void decode_kernel(DecodeP
         acc[3][2 * e] = fmaf(w.w, c2.x, acc[3][2 * e]);
         acc[3][2 * e + 1] = fmaf(w.w, c2.y, acc[3][2 * e + 1]);
       }
-      if ((u & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+    };
+    if constexpr (VCHUNK) {
+      constexpr int VC = 4;
+      auto load_v = [&](int u0, uint32_t (&dst)[VC][2]) {
+#pragma unroll
+        for (int q = 0; q < VC; ++q) {
+          int64_t vt = tile + (int64_t)(u0 + q) * TS + ts;
+          vt = vt < t1 ? vt : t0;
+          const uint32_t* vr = reinterpret_cast<const uint32_t*>(p.vidx + (kv_base + vt) * VROW);
+          dst[q][0] = vr[vw0];
+          dst[q][1] = vstraddle ? vr[vw1] : 0u;
+        }
+      };
+      uint32_t vnext[VC][2];
+      load_v(0, vnext);
+#pragma unroll 1
+      for (int c = 0; c < TPL / VC; ++c) {
+        uint32_t vc4[VC][2];
+#pragma unroll
+        for (int q = 0; q < VC; ++q) {
+          vc4[q][0] = vnext[q][0];
+          vc4[q][1] = vnext[q][1];
+        }
+        if (c + 1 < TPL / VC) load_v((c + 1) * VC, vnext);
+#pragma unroll
+        for (int q = 0; q < VC; ++q)
+          accum(c * VC + q, vstraddle ? __builtin_amdgcn_alignbit(vc4[q][1], vc4[q][0], vbit0 & 31)
+                                      : (vc4[q][0] >> (vbit0 & 31)));
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < TPL; ++u) {
+        uint32_t bits;
+        if constexpr (VST) {
+          const uint32_t* vr = s_vst + (wave * kWave + u * TS + ts) * VSTR;
+          bits = __builtin_amdgcn_alignbit(vr[vw1], vr[vw0], vbit0 & 31);
+        } else {
+          bits = vstraddle ? __builtin_amdgcn_alignbit(vwr[u][1], vwr[u][0], vbit0 & 31)
+                           : (vwr[u][0] >> (vbit0 & 31));
+        }
+        accum(u, bits);
+        if ((u & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+      }
     }
     __builtin_amdgcn_wave_barrier();
   }

@@ -79,6 +79,10 @@ def test_attend_gqa_decode_full():
     (1, 16, 1, 4099, 2, 128, 3, 4),
     (1, 4, 2, 700, 5, 64, 3, 3),
     (2, 2, 2, 300, 17, 64, 2, 2),
+    # 3-bit values with 1- and 3-bit key tables at d = 128: value words
+    # loaded four tokens at a time
+    (1, 8, 2, 1025, 1, 128, 2, 3),
+    (2, 8, 2, 777, 2, 128, 4, 3),
 ])
 def test_attend_shapes(B, Hq, Hkv, ctx, nq, d, kb, vb):
     say("attend B=%d Hq=%d Hkv=%d ctx=%d nq=%d d=%d kb=%d vb=%d" % (B, Hq, Hkv, ctx, nq, d, kb, vb))
