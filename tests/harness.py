@@ -18,7 +18,12 @@ Readings where the page is silent:
   (relMSE, 1 - cos) from the error-free point (0, 0).
 * The two schemes at a budget of b bits per coordinate: TQ-KV = mse keys
   and values at b bits; TQ-QKV = prod keys (b - 1 bit table + 1-bit QJL)
-  and mse values at b bits.
+  and mse values at b bits.  Two more at 2.5 bits: FQ = FibQuant k = 2 at
+  N = 32 for keys and values; SPLIT = the outlier-channel split, 3 bits on
+  the 64 channels of largest mean square (measured on the tensor itself)
+  and 2 on the rest, prod keys and mse values (both sides order the
+  channels with their own implementation of the rule, and the decoded
+  channels are put back in the original order).
 * The reference attention is plain softmax attention in fp64 on the
   unquantized K, V (scale 1 / sqrt(d)); the codec's attention output is the
   same attention on the decoded vectors (equal to attention from codes, a
@@ -35,6 +40,7 @@ import synth
 from synth import regimes
 
 SCHEMES = ("TQ-KV", "TQ-QKV")
+SCHEMES_25 = ("FQ", "SPLIT")          # 2.5 bits per coordinate
 
 
 def rel_mse(x, xh):
@@ -76,9 +82,43 @@ def data(regime, seed, n=512, d=128, n_q=4):
 
 
 def draws_for(scheme, rng, d):
+    """The codec's own draws: (K, V) sign flips and S; for SPLIT one pair
+    per 64-channel half ((K hi, K lo), (V hi, V lo))."""
+    if scheme == "SPLIT":
+        kd = (synth.codec_draws(rng, d // 2, m=d // 2), synth.codec_draws(rng, d // 2, m=d // 2))
+        vd = (synth.codec_draws(rng, d // 2), synth.codec_draws(rng, d // 2))
+        return kd, vd
     kd = synth.codec_draws(rng, d, m=d if scheme == "TQ-QKV" else 0)
     vd = synth.codec_draws(rng, d)
     return kd, vd
+
+
+_FQ_BOOK = {}
+
+
+def fq_book(d, n_codes=32):
+    if (d, n_codes) not in _FQ_BOOK:
+        _FQ_BOOK[(d, n_codes)] = oracle.fibquant_codebook(d, n_codes)
+    return _FQ_BOOK[(d, n_codes)]
+
+
+def split_half(draws, bits, prod):
+    if prod:
+        c, t = oracle.codebook(draws.flip.size, bits - 1)
+        return {"signs": draws.flip, "centroids": c, "thresholds": t,
+                "S": draws.S.astype(np.float64)}
+    c, t = oracle.codebook(draws.flip.size, bits)
+    return {"signs": draws.flip, "centroids": c, "thresholds": t}
+
+
+def _split_decoded(x, draws, prod):
+    perm = oracle.outlier_permutation(x, x.shape[1] // 2)
+    hi, lo = split_half(draws[0], 3, prod), split_half(draws[1], 2, prod)
+    xp = x[:, perm]
+    enc = (oracle.encode_split_prod if prod else oracle.encode_split_mse)(xp, x.shape[1] // 2, hi, lo)
+    out = np.empty_like(xp)
+    out[:, perm] = oracle.decode_split(enc, hi, lo)
+    return out
 
 
 def metrics(k, v, q, kh, vh):
@@ -94,6 +134,13 @@ def oracle_decoded(scheme, bits, k, v, kd, vd, qjl_factor_scale=1.0):
     wrong QJL constant (used only to show the KS test's power)."""
     d = k.shape[-1]
     k64, v64 = k.astype(np.float64), v.astype(np.float64)
+    if scheme == "FQ":
+        code = fq_book(d)
+        ik, nk, _ = oracle.encode_vq(k64, kd.flip, code)
+        iv, nv, _ = oracle.encode_vq(v64, vd.flip, code)
+        return oracle.decode_vq(ik, nk, kd.flip, code), oracle.decode_vq(iv, nv, vd.flip, code)
+    if scheme == "SPLIT":
+        return _split_decoded(k64, kd, True), _split_decoded(v64, vd, False)
     if scheme == "TQ-QKV":
         c, t = oracle.codebook(d, bits - 1)
         S = kd.S.astype(np.float64)

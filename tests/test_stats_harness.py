@@ -73,6 +73,19 @@ def test_ks_two_rng_families_agree_on_the_oracle(regime, scheme):
         assert H.ks_p(a[name], b[name]) > 1e-3, name
 
 
+@pytest.mark.parametrize("scheme", H.SCHEMES_25)
+def test_ks_two_rng_families_agree_at_two_and_a_half_bits(scheme):
+    """The same for FibQuant at N = 32 and the 3 / 2 outlier split, whose
+    errors sit between the whole-codec 2- and 3-bit ones."""
+    a = H.oracle_run("heavy_tailed", scheme, 3, SEEDS, "pcg64")
+    b = H.oracle_run("heavy_tailed", scheme, 3, SEEDS, "mt19937")
+    for name in a:
+        assert H.ks_p(a[name], b[name]) > 1e-3, name
+    lo = H.oracle_run("heavy_tailed", "TQ-KV", 2, range(8), "pcg64")
+    hi = H.oracle_run("heavy_tailed", "TQ-KV", 3, range(8), "pcg64")
+    assert hi["relmse_v"].mean() < a["relmse_v"].mean() < lo["relmse_v"].mean()
+
+
 def test_ks_separates_a_planted_wrong_qjl_constant():
     """A plausible mistake planted in a copy of the oracle -- the QJL scale
     sqrt(pi/2)/m off by 25% -- is separated from the correct codec."""
