@@ -274,6 +274,12 @@ __global__ __launch_bounds__(kVqWaves * kWave, 2) void decode_vq_kernel(VqParams
   constexpr int RB = 2 * HB;
   constexpr int HWD = (HB + 3) / 4;
   __shared__ float2 s_cw[N];
+  // each wave's 32 output rows, staged so that the stores of the tile (one
+  // contiguous block of 32 rows) are whole 1 KB chunks; rows padded by 16
+  // bytes against bank conflicts
+  constexpr int RBYTES = D * (F16 ? 2 : 4);
+  constexpr int PITCH = RBYTES + 16;
+  __shared__ __align__(16) unsigned char s_out[kVqWaves][32 * PITCH];
   const VqParams* kp = (const VqParams*)__builtin_amdgcn_kernarg_segment_ptr();
   for (int n = threadIdx.x; n < N; n += blockDim.x)
     s_cw[n] = make_float2(kp->codewords[2 * n], kp->codewords[2 * n + 1]);
@@ -299,8 +305,6 @@ __global__ __launch_bounds__(kVqWaves * kWave, 2) void decode_vq_kernel(VqParams
     nnorm = p.norm_in[r];
   }
   for (; tile < ntiles; tile += tstride) {
-    const int64_t row = row_of(tile);
-    const bool valid = tile * 32 + (lane & 31) < p.n_rows;
     uint32_t bits[HWD];
 #pragma unroll
     for (int j = 0; j < HWD; ++j) bits[j] = nbits[j];
@@ -327,24 +331,40 @@ __global__ __launch_bounds__(kVqWaves * kWave, 2) void decode_vq_kernel(VqParams
 #pragma unroll
     for (int i = 0; i < HALF; ++i)
       w[i] *= __uint_as_float(((fl[i >> 5] << (31 - (i & 31))) & 0x80000000u) | __float_as_uint(sc));
-    if (valid) {
+    unsigned char* stage = s_out[wave];
+    {
+      uint4* dst = reinterpret_cast<uint4*>(stage + (lane & 31) * PITCH + h * (RBYTES / 2));
       if constexpr (F16) {
-        _Float16* dst = reinterpret_cast<_Float16*>(p.out) + row * D + h * HALF;
 #pragma unroll
         for (int q = 0; q < HALF / 8; ++q) {
           uint32_t o[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j)
             o[j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(w[8 * q + 2 * j], w[8 * q + 2 * j + 1]));
-          reinterpret_cast<uint4*>(dst)[q] = make_uint4(o[0], o[1], o[2], o[3]);
+          dst[q] = make_uint4(o[0], o[1], o[2], o[3]);
         }
       } else {
-        float* dst = reinterpret_cast<float*>(p.out) + row * D + h * HALF;
 #pragma unroll
         for (int q = 0; q < HALF / 4; ++q)
-          reinterpret_cast<float4*>(dst)[q] = make_float4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
+          dst[q] = make_uint4(__float_as_uint(w[4 * q]), __float_as_uint(w[4 * q + 1]),
+                              __float_as_uint(w[4 * q + 2]), __float_as_uint(w[4 * q + 3]));
       }
     }
+    // LDS operations of one wave complete in order: no workgroup barrier
+    __builtin_amdgcn_wave_barrier();
+    {
+      constexpr int CPR = RBYTES / 16;                      // 16-byte chunks per row
+      const int64_t row0 = tile * 32;
+      const int64_t rows = (p.n_rows - row0) < 32 ? (p.n_rows - row0) : 32;
+      uint4* gdst = reinterpret_cast<uint4*>(reinterpret_cast<unsigned char*>(p.out) + row0 * RBYTES);
+#pragma unroll
+      for (int k = 0; k < 32 * CPR / kWave; ++k) {
+        const int c = lane + kWave * k;
+        const int r = c / CPR, col = c % CPR;
+        if (r < rows) gdst[c] = *reinterpret_cast<const uint4*>(stage + r * PITCH + col * 16);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
