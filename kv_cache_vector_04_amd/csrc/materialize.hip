@@ -70,6 +70,13 @@ __global__ __launch_bounds__(kMatWaves * kWave, MatLaunch<D>::kMinWavesPerEU) vo
   __shared__ float s_cent[16];
   __shared__ uint4 s_pm[PROD ? 256 : 1];            // 8 signs -> 8 fp16 (+1 / -1)
   __shared__ uint4 s_st[PROD ? FRAGS * 2 * kWave : 1];
+  // mse: each wave's 32 output rows staged in LDS (rows padded by 16 bytes)
+  // so that a row's bytes are stored in whole 16-byte chunks by consecutive
+  // lanes; prod keeps half-row stores (its S fragments fill the LDS)
+  constexpr bool STAGE = !PROD;
+  constexpr int RBYTES = D * (F16 ? 2 : 4);
+  constexpr int PITCH = RBYTES + 16;
+  __shared__ __align__(16) unsigned char s_out[STAGE ? kMatWaves : 1][STAGE ? 32 * PITCH : 16];
 
   const int tid = threadIdx.x;
   const MatParams* kp = (const MatParams*)__builtin_amdgcn_kernarg_segment_ptr();
@@ -203,7 +210,41 @@ __global__ __launch_bounds__(kMatWaves * kWave, MatLaunch<D>::kMinWavesPerEU) vo
       const uint32_t fb = fl[i >> 5] << (31 - (i & 31));
       w[i] *= __uint_as_float((fb & 0x80000000u) | __float_as_uint(sc));
     }
-    if (valid) {
+    if constexpr (STAGE) {
+      unsigned char* stage = s_out[wave];
+      uint4* sdst = reinterpret_cast<uint4*>(stage + (lane & 31) * PITCH + h * (RBYTES / 2));
+      if constexpr (F16) {
+#pragma unroll
+        for (int q = 0; q < HALF / 8; ++q) {
+          uint32_t o[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            o[j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(w[8 * q + 2 * j], w[8 * q + 2 * j + 1]));
+          sdst[q] = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < HALF / 4; ++q)
+          sdst[q] = make_uint4(__float_as_uint(w[4 * q]), __float_as_uint(w[4 * q + 1]),
+                               __float_as_uint(w[4 * q + 2]), __float_as_uint(w[4 * q + 3]));
+      }
+      // LDS operations of one wave complete in order: no workgroup barrier
+      __builtin_amdgcn_wave_barrier();
+      constexpr int CPR = RBYTES / 16;                      // 16-byte chunks per row
+      const int64_t row0 = tile * 32;
+      const int64_t rows = (p.n_rows - row0) < 32 ? (p.n_rows - row0) : 32;
+      const int64_t pitch_out = p.out_stride * (F16 ? 2 : 4);
+      unsigned char* gout = reinterpret_cast<unsigned char*>(p.out) + row0 * pitch_out;
+#pragma unroll
+      for (int k = 0; k < 32 * CPR / kWave; ++k) {
+        const int c = lane + kWave * k;
+        const int r = c / CPR, col = c % CPR;
+        if (r < rows)
+          *reinterpret_cast<uint4*>(gout + r * pitch_out + col * 16) =
+              *reinterpret_cast<const uint4*>(stage + r * PITCH + col * 16);
+      }
+      __builtin_amdgcn_wave_barrier();
+    } else if (valid) {
       if constexpr (F16) {
         _Float16* dst = reinterpret_cast<_Float16*>(p.out) + row * p.out_stride + h * HALF;
 #pragma unroll
