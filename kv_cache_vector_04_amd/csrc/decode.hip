@@ -222,23 +222,14 @@ __global__ __launch_bounds__(DecWaves<CBV>::kThreads) void decode_kernel(DecodeP
   const int vw1 = (vw0 + 1) < VW ? (vw0 + 1) : (VW - 1);
   const bool vstraddle = (vbit0 & 31) + 8 * CBV > 32;
 
-  // the planes from this range's first token (uniform bases), addressed with
-  // one 32-bit token offset per lane
-  const int64_t rb = kv_base + t0;
-  const uint8_t* const kidx0 = p.kidx + rb * KROW;
-  const uint8_t* const kqjl0 = p.kqjl + rb * NB;
-  const float* const knorm0 = p.knorm + rb;
-  const float* const krnorm0 = p.krnorm + rb;
-  const float* const vnorm0 = p.vnorm + rb;
-  const uint8_t* const vidx0 = p.vidx + rb * VROW;
   auto load_tile = [&](int64_t tile, TileRegs<WK, NB / 4>& R) {
     const int64_t tok = tile + lane;
-    const uint32_t rel = tok < t1 ? (uint32_t)(tok - t0) : 0u;
-    load_words<WK, Gm::KALIGN>(kidx0 + rel * KROW, R.kw);
-    load_words<NB / 4, (NB % 16 == 0) ? 16 : 8>(kqjl0 + rel * NB, R.sb);
-    R.nuk = knorm0[rel] * p.scale;
-    R.gk = krnorm0[rel] * p.qjl_scale;
-    R.nuv = vnorm0[rel];
+    const int64_t kr = kv_base + (tok < t1 ? tok : t0);
+    load_words<WK, Gm::KALIGN>(p.kidx + kr * KROW, R.kw);
+    load_words<NB / 4, (NB % 16 == 0) ? 16 : 8>(p.kqjl + kr * NB, R.sb);
+    R.nuk = p.knorm[kr] * p.scale;
+    R.gk = p.krnorm[kr] * p.qjl_scale;
+    R.nuv = p.vnorm[kr];
   };
 
   // first tile's key codes in flight during the set-up
@@ -412,14 +403,14 @@ __global__ __launch_bounds__(DecWaves<CBV>::kThreads) void decode_kernel(DecodeP
     uint32_t vwr[VCHUNK ? 1 : TPL][2];
     uint32_t vrow[VST ? VW : 1];   // 3-bit codes: the lane's own token row, staged to LDS
     if constexpr (VST) {
-      const uint32_t vt = valid ? (uint32_t)(tok - t0) : 0u;
-      load_words<VW, (VROW % 16 == 0) ? 16 : 8>(vidx0 + vt * VROW, vrow);
+      const int64_t vt = valid ? tok : t0;
+      load_words<VW, (VROW % 16 == 0) ? 16 : 8>(p.vidx + (kv_base + vt) * VROW, vrow);
     } else if constexpr (!VCHUNK) {
 #pragma unroll
       for (int u = 0; u < TPL; ++u) {
         int64_t vt = tile + (int64_t)u * TS + ts;
-        const uint32_t rel = vt < t1 ? (uint32_t)(vt - t0) : 0u;
-        const uint32_t* vr = reinterpret_cast<const uint32_t*>(vidx0 + rel * VROW);
+        vt = vt < t1 ? vt : t0;
+        const uint32_t* vr = reinterpret_cast<const uint32_t*>(p.vidx + (kv_base + vt) * VROW);
         vwr[u][0] = vr[vw0];
         vwr[u][1] = vstraddle ? vr[vw1] : 0u;
       }
@@ -497,9 +488,9 @@ __global__ __launch_bounds__(DecWaves<CBV>::kThreads) void decode_kernel(DecodeP
       auto load_v = [&](int u0, uint32_t (&dst)[VC][2]) {
 #pragma unroll
         for (int q = 0; q < VC; ++q) {
-          const int64_t vt = tile + (int64_t)(u0 + q) * TS + ts;
-          const uint32_t rel = vt < t1 ? (uint32_t)(vt - t0) : 0u;
-          const uint32_t* vr = reinterpret_cast<const uint32_t*>(vidx0 + rel * VROW);
+          int64_t vt = tile + (int64_t)(u0 + q) * TS + ts;
+          vt = vt < t1 ? vt : t0;
+          const uint32_t* vr = reinterpret_cast<const uint32_t*>(p.vidx + (kv_base + vt) * VROW);
           dst[q][0] = vr[vw0];
           dst[q][1] = vstraddle ? vr[vw1] : 0u;
         }
