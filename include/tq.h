@@ -342,8 +342,9 @@ int tq_attend_decode(const tq_codec* kc, const tq_codec* vc, const void* q,
  *   scale  0 selects 1/sqrt(128)
  *   out, scores_out, workspace: as tq_attend_decode, with the workspace size
  *       tq_attend_decode_workspace(batch, n_q, hq, hkv, ctx, 128)
- * (hq / hkv) * n_q <= 16 (larger: TQ_ERR_UNSUPPORTED).  Returns TQ_OK,
- * TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_WORKSPACE or TQ_ERR_HIP. */
+ * (hq / hkv) * n_q <= 16 and ctx <= 2^26 (otherwise TQ_ERR_UNSUPPORTED).
+ * Returns TQ_OK, TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_WORKSPACE or
+ * TQ_ERR_HIP. */
 int tq_attend_split(const tq_split_codec* kc, const tq_split_codec* vc, const void* q,
                     int q_dtype, int batch, int n_q, int hq, int hkv, const tq_packed* k,
                     const tq_packed* v, int64_t ctx, float scale, float* out,

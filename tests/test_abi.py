@@ -258,6 +258,7 @@ def test_attend_split_validation_before_launch(L):
     assert call(ctx=0) == tq.TQ_ERR_INVALID_ARG
     assert call(scale=-1.0) == tq.TQ_ERR_INVALID_ARG
     assert call(hq=64, hkv=2) == tq.TQ_ERR_UNSUPPORTED          # 32 query rows per KV head
+    assert call(ctx=(1 << 26) + 1) == tq.TQ_ERR_UNSUPPORTED      # past the 32-bit token offsets
     assert call(k=ctypes.byref(sc(tq.TQ_PROD, 4, 2))) == tq.TQ_ERR_UNSUPPORTED   # widths (3, 1)
     assert call(k=V, v=K) == tq.TQ_ERR_INVALID_ARG              # mse keys lack QJL planes
     assert call(ws=None) == tq.TQ_ERR_WORKSPACE
