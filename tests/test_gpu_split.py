@@ -191,6 +191,26 @@ def test_split_attention_from_codes(b_hi, b_lo, G, n_q):
             check_rows(scores[b, g * G:(g + 1) * G].reshape(G * n_q, ctx), s_want, tol=1e-3)
 
 
+@pytest.mark.parametrize("ctx", [1, 63])
+def test_split_attention_short_context(ctx):
+    """One partial tile (and a single token): outputs against the oracle."""
+    say("attend split ctx=%d" % ctx)
+    rng = np.random.default_rng(800 + ctx)
+    hkv, G = 2, 4
+    k = rng.standard_normal((hkv * ctx, 128)).astype(np.float16)
+    v = rng.standard_normal((hkv * ctx, 128)).astype(np.float16)
+    q = rng.standard_normal((1, hkv * G, 1, 128)).astype(np.float16)
+    ks, vs, ko, vo = make(rng, 4, 3)
+    kp, vp = tq.encode_split(ks, vs, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda())
+    out = to_np(tq.attend_split(ks, vs, torch.from_numpy(q).cuda(), kp, vp, ctx, hkv)).astype(np.float64)
+    torch.cuda.synchronize()
+    for g in range(hkv):
+        gk, gv = oracle_split_codes(kp, vp, ks, vs, np.arange(g * ctx, (g + 1) * ctx))
+        qq = q[0, g * G:(g + 1) * G, 0].astype(np.float64)
+        check_rows(out[0, g * G:(g + 1) * G, 0], SP.attention_split(qq, gk, gv, 64, ko[0], ko[1], vo[0], vo[1]),
+                   tol=1e-3)
+
+
 def test_split_attention_validation():
     rng = np.random.default_rng(3)
     ks, vs, _, _ = make(rng, 3, 2)

@@ -166,6 +166,22 @@ def test_vq_empty_input():
     assert idx.shape == (0, 40) and norm.shape == (0,) and out.shape == (0, 128)
 
 
+def test_vq_single_row_with_table():
+    """One row (one partial tile) through the cell-table encoder and the
+    staged decoder."""
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((1, 128)).astype(np.float16)
+    flip = synth.codec_draws(rng, 128).flip
+    codec = tq.VQCodec(128, 64, flip, search=True)
+    gi, gn, y32, y16 = run(codec, x)
+    code = book(128, 64)
+    oi, onu, z = oracle.encode_vq(x.astype(np.float64), flip, code)
+    g = oracle.unpack_vq(gi, 128, 64)
+    check_vq_codes(g, oi, z, code)
+    check_norm(gn, onu)
+    check_rows(y32.astype(np.float64), oracle.decode_vq(g, gn, flip, code), tol=F32_ROW_RTOL)
+
+
 def test_vq_full_size_gqa_keys_sampled():
     """The 8 x 32768 x 128 keys of the GQA decode workload (fp16 Student-t,
     outlier channels) at N = 32 (2.5 bits per coordinate), in one launch;
