@@ -34,6 +34,7 @@
 // 16 (l/32) + 0..15 of the 32-row tile: each lane half collects 16
 // consecutive sign bits, and one more swap puts every word on its row.
 
+#include <atomic>
 #include <cmath>
 #include <cstring>
 
@@ -837,17 +838,19 @@ __global__ __launch_bounds__((kKVKeyWaves + kKVValWaves) * kWave, 3) void encode
 template <int D, int CB, bool PROD>
 static hipError_t run_half(const EncodeParams& p, hipStream_t stream) {
   constexpr int kHalfWaves = HalfLaunch<PROD>::kWaves;
-  static int per_cu = 0;
-  if (per_cu == 0) {
+  // occupancy depends only on the kernel's resources (one code object for
+  // every device): computed once, read by any host thread
+  static std::atomic<int> per_cu{0};
+  if (per_cu.load(std::memory_order_relaxed) == 0) {
     int nb = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, encode_half_kernel<D, CB, PROD>,
                                                      kHalfWaves * kWave, 0) != hipSuccess || nb < 1)
       nb = 1;
-    per_cu = nb;
+    per_cu.store(nb, std::memory_order_relaxed);
   }
   const int64_t ntiles = (p.n_rows + 31) / 32;
   int64_t blocks = (ntiles + kHalfWaves - 1) / kHalfWaves;
-  const int64_t cap = (int64_t)device_cu_count() * per_cu;
+  const int64_t cap = (int64_t)device_cu_count() * per_cu.load(std::memory_order_relaxed);
   if (blocks > cap) blocks = cap;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL((encode_half_kernel<D, CB, PROD>), dim3((unsigned)blocks),
@@ -984,19 +987,21 @@ hipError_t launch_encode(const tq_codec& c, const void* x, int dtype, int64_t n_
 
 template <int D, int CBK, int CBV>
 static hipError_t run_kv_half(const EncodeKVParams& pp, hipStream_t stream) {
-  static int per_cu = 0;
+  // occupancy depends only on the kernel's resources (one code object for
+  // every device): computed once, read by any host thread
+  static std::atomic<int> per_cu{0};
   constexpr int kThreads = (kKVKeyWaves + kKVValWaves) * kWave;
-  if (per_cu == 0) {
+  if (per_cu.load(std::memory_order_relaxed) == 0) {
     int nb = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, encode_kv_half_kernel<D, CBK, CBV>, kThreads, 0) !=
             hipSuccess || nb < 1)
       nb = 1;
-    per_cu = nb;
+    per_cu.store(nb, std::memory_order_relaxed);
   }
   // enough workgroups for every key wave to have a tile, at most what fits
   const int64_t ntiles = (pp.k.n_rows + 31) / 32;
   int64_t blocks = (ntiles + kKVKeyWaves - 1) / kKVKeyWaves;
-  const int64_t cap = (int64_t)device_cu_count() * per_cu;
+  const int64_t cap = (int64_t)device_cu_count() * per_cu.load(std::memory_order_relaxed);
   if (blocks > cap) blocks = cap;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL((encode_kv_half_kernel<D, CBK, CBV>), dim3((unsigned)blocks), dim3(kThreads), 0,

@@ -25,6 +25,7 @@
 // - D and nu / sqrt(d) in one multiply per coordinate (the sign bit of the
 //   scale is set from the flip bit), then fp16 or fp32 stores.
 
+#include <atomic>
 #include <cmath>
 
 #include "device_common.hpp"
@@ -267,17 +268,19 @@ __global__ __launch_bounds__(kMatWaves * kWave, MatLaunch<D>::kMinWavesPerEU) vo
 
 template <int D, int CB, bool PROD, bool F16>
 static hipError_t run_mat(const MatParams& p, hipStream_t stream) {
-  static int per_cu = 0;
-  if (per_cu == 0) {
+  // occupancy depends only on the kernel's resources (one code object for
+  // every device): computed once, read by any host thread
+  static std::atomic<int> per_cu{0};
+  if (per_cu.load(std::memory_order_relaxed) == 0) {
     int nb = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, materialize_kernel<D, CB, PROD, F16>,
                                                      kMatWaves * kWave, 0) != hipSuccess || nb < 1)
       nb = 1;
-    per_cu = nb;
+    per_cu.store(nb, std::memory_order_relaxed);
   }
   const int64_t ntiles = (p.n_rows + 31) / 32;
   int64_t blocks = (ntiles + kMatWaves - 1) / kMatWaves;
-  const int64_t cap = (int64_t)device_cu_count() * per_cu;
+  const int64_t cap = (int64_t)device_cu_count() * per_cu.load(std::memory_order_relaxed);
   if (blocks > cap) blocks = cap;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL((materialize_kernel<D, CB, PROD, F16>), dim3((unsigned)blocks),
