@@ -4,8 +4,10 @@ Argument marshalling only: every step of encode, attention and search runs
 in the HIP kernels behind the C ABI declared in include/tq.h.  PyTorch
 provides device memory and the current stream; nothing here computes.
 
-The library must be built (``python -m kv_cache_vector_04_amd.build``);
-importing this module fails loudly when it is missing.
+The library must be built (``python -m kv_cache_vector_04_amd.build``):
+without it the first call into the binding raises ImportError (there is no
+fallback path).  The import itself does not load it, so that tests which
+import this module fail, rather than skip, when it is missing.
 """
 
 import ctypes

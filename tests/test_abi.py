@@ -330,3 +330,14 @@ def test_sizes_closed_form():
     assert 128 * 4 // 8 + 4 == 68                 # value, mse b = 4
     assert 64 * 2 // 8 + 64 // 8 + 8 == 32        # ESM-2 key, prod b = 3
     assert 1536 * 1 // 8 + 1536 // 8 + 8 == 392   # vector search, prod b = 2
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    """No CPU fallback: without libtq.so the first call raises ImportError."""
+    import kv_cache_vector_04_amd as tq
+    monkeypatch.setattr(tq, "_lib", None)
+    monkeypatch.setattr(tq, "LIB_PATH", "/nonexistent/libtq.so")
+    with pytest.raises(ImportError, match="no fallback"):
+        tq.lib()
+    with pytest.raises(ImportError):
+        tq.build_codebook(128, 3)
