@@ -89,6 +89,17 @@ def test_attend_shapes(B, Hq, Hkv, ctx, nq, d, kb, vb):
     _run(B, Hq, Hkv, ctx, nq, d, kb, vb, seed=ctx + nq + d)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("kb", [2, 3, 4, 5])
+@pytest.mark.parametrize("vb", [1, 2, 3, 4])
+def test_attend_every_bit_width_pair(d, kb, vb):
+    """Every key width (1..4 table bits + the QJL bit) with every value
+    width: each pair is its own kernel instance; two full tiles plus a
+    ragged tail."""
+    say("attend every width d=%d kb=%d vb=%d" % (d, kb, vb))
+    _run(1, 4, 2, 130, 1, d, kb, vb, seed=1000 + 10 * kb + vb + d)
+
+
 def test_attend_heavy_tails():
     say("attend Student-t(3) 8x2 heads ctx 5000")
     _run(1, 8, 2, 5000, 1, 128, 4, 4, seed=11, dist="t")
