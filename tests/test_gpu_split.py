@@ -44,14 +44,18 @@ def oracle_half(draws, bits, prod):
     return {"signs": draws.flip, "centroids": c, "thresholds": t}
 
 
-def make(rng, b_hi, b_lo):
+def make(rng, b_hi, b_lo, vb_hi=None, vb_lo=None):
+    """Key and value split codecs: keys at (b_hi, b_lo), values at
+    (vb_hi, vb_lo) (the key rates unless given)."""
+    vb_hi = b_hi if vb_hi is None else vb_hi
+    vb_lo = b_lo if vb_lo is None else vb_lo
     kh, kdh = half_codec(rng, b_hi, True)
     kl, kdl = half_codec(rng, b_lo, True)
-    vh, vdh = half_codec(rng, b_hi, False)
-    vl, vdl = half_codec(rng, b_lo, False)
+    vh, vdh = half_codec(rng, vb_hi, False)
+    vl, vdl = half_codec(rng, vb_lo, False)
     ks, vs = tq.SplitCodec(kh, kl), tq.SplitCodec(vh, vl)
     ko = (oracle_half(kdh, b_hi, True), oracle_half(kdl, b_lo, True))
-    vo = (oracle_half(vdh, b_hi, False), oracle_half(vdl, b_lo, False))
+    vo = (oracle_half(vdh, vb_hi, False), oracle_half(vdl, vb_lo, False))
     return ks, vs, ko, vo
 
 
@@ -189,6 +193,29 @@ def test_split_attention_from_codes(b_hi, b_lo, G, n_q):
             check_rows(got, want, tol=1e-3)
             s_want = SP.estimate_split(qq, gk, 64, ko[0], ko[1]) / np.sqrt(128.0)
             check_rows(scores[b, g * G:(g + 1) * G].reshape(G * n_q, ctx), s_want, tol=1e-3)
+
+
+@pytest.mark.parametrize("kr,vr", [((3, 2), (4, 3)), ((4, 3), (3, 2))])
+def test_split_attention_mixed_rates(kr, vr):
+    """Keys and values at different split rates (2.5 / 3.5 and 3.5 / 2.5
+    bits): the kernel instances the matched-rate cases do not reach."""
+    say("attend split K %d/%d V %d/%d" % (kr + vr))
+    rng = np.random.default_rng(700 + 10 * kr[0] + vr[0])
+    hkv, G, ctx = 2, 4, 1500 + 11
+    k = rng.standard_t(3, (hkv * ctx, 128)) * rng.uniform(0.2, 3, (hkv * ctx, 1))
+    k[:, [2, 40]] *= 8.0
+    v = rng.standard_normal((hkv * ctx, 128))
+    q = rng.standard_normal((1, hkv * G, 1, 128)).astype(np.float16)
+    ks, vs, ko, vo = make(rng, kr[0], kr[1], vr[0], vr[1])
+    kp, vp = tq.encode_split(ks, vs, torch.from_numpy(k.astype(np.float16)).cuda(),
+                             torch.from_numpy(v.astype(np.float16)).cuda())
+    out = to_np(tq.attend_split(ks, vs, torch.from_numpy(q).cuda(), kp, vp, ctx, hkv)).astype(np.float64)
+    torch.cuda.synchronize()
+    for g in range(hkv):
+        gk, gv = oracle_split_codes(kp, vp, ks, vs, np.arange(g * ctx, (g + 1) * ctx))
+        qq = q[0, g * G:(g + 1) * G, 0].astype(np.float64)
+        check_rows(out[0, g * G:(g + 1) * G, 0], SP.attention_split(qq, gk, gv, 64, ko[0], ko[1], vo[0], vo[1]),
+                   tol=1e-3)
 
 
 @pytest.mark.parametrize("ctx", [1, 63])
