@@ -89,15 +89,17 @@ def test_attend_shapes(B, Hq, Hkv, ctx, nq, d, kb, vb):
     _run(B, Hq, Hkv, ctx, nq, d, kb, vb, seed=ctx + nq + d)
 
 
+@pytest.mark.parametrize("nq", [1, 9])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("kb", [2, 3, 4, 5])
 @pytest.mark.parametrize("vb", [1, 2, 3, 4])
-def test_attend_every_bit_width_pair(d, kb, vb):
+def test_attend_every_bit_width_pair(d, kb, vb, nq):
     """Every key width (1..4 table bits + the QJL bit) with every value
     width: each pair is its own kernel instance; two full tiles plus a
-    ragged tail."""
-    say("attend every width d=%d kb=%d vb=%d" % (d, kb, vb))
-    _run(1, 4, 2, 130, 1, d, kb, vb, seed=1000 + 10 * kb + vb + d)
+    ragged tail.  nq = 1 gives 2 query rows per KV head (the few-row decode
+    kernel), nq = 9 gives 18 (the many-query kernels)."""
+    say("attend every width d=%d kb=%d vb=%d nq=%d" % (d, kb, vb, nq))
+    _run(1, 4, 2, 130, nq, d, kb, vb, seed=1000 + 10 * kb + vb + d + 7 * nq)
 
 
 def test_attend_heavy_tails():
