@@ -66,6 +66,23 @@ def test_inner_product_modes(d, mode, bits):
     check_rows(est, ref)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("mode,bits", [(0, 1), (0, 2), (0, 3), (0, 4), (1, 2), (1, 3), (1, 4), (1, 5)])
+def test_inner_product_every_width(d, mode, bits):
+    """Every code width at both dimensions, a ragged row count and a
+    query count that is not a multiple of any block size."""
+    say("scan every width d=%d mode=%d bits=%d" % (d, mode, bits))
+    rng = np.random.default_rng(5000 + 10 * d + 3 * mode + bits)
+    n, nq = 700 + 3, 5
+    keys = (rng.standard_normal((n, d)) * rng.uniform(0.1, 4, (n, 1))).astype(np.float32)
+    queries = rng.standard_normal((nq, d)).astype(np.float32)
+    draws = synth.codec_draws(rng, d, m=d if mode else 0)
+    codec, pk = _setup(keys, queries, draws, d, mode, bits)
+    est = to_np(tq.inner_product(codec, torch.from_numpy(queries).cuda(), pk, n)).astype(np.float64)
+    ref, _ = _oracle_scores(queries, pk, codec, draws)
+    check_rows(est, ref)
+
+
 def _check_topk(ids, vals, ref, k):
     """GPU ids must be the oracle's top-k over the GPU codes, except swaps
     among entries whose oracle scores differ by <= 1e-3 * max |score|."""
