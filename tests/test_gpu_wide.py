@@ -64,7 +64,7 @@ def test_wide_encode_prod_b2_fp32():
     print(rep)
 
 
-@pytest.mark.parametrize("mode,bits", [(0, 1), (0, 2), (0, 3), (0, 4), (1, 3), (1, 4)])
+@pytest.mark.parametrize("mode,bits", [(0, 1), (0, 2), (0, 3), (0, 4), (1, 3), (1, 4), (1, 5)])
 def test_wide_encode_widths_fp16(mode, bits):
     say("d=1536 encode mode=%d bits=%d fp16, ragged 261 rows with a zero row" % (mode, bits))
     rng = np.random.default_rng(100 + 10 * mode + bits)
@@ -108,7 +108,7 @@ def _oracle_scores(q, pk, codec, draws, rows=None):
     return oracle.inner_product_matrix(np.asarray(q, dtype=np.float64), g, book)
 
 
-@pytest.mark.parametrize("mode,bits", [(1, 2), (0, 1), (1, 3), (0, 3)])
+@pytest.mark.parametrize("mode,bits", [(1, 2), (0, 1), (1, 3), (0, 3), (0, 2), (1, 4), (0, 4), (1, 5)])
 def test_wide_scan_and_top10(mode, bits):
     p = _params()
     n, nq = 5000 + 37, 40
