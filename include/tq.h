@@ -197,7 +197,8 @@ typedef struct tq_split_codec {
  * channels of largest mean square over the calibration rows x (host,
  * n_rows x d fp32, row-major), ascending, then the other channels,
  * ascending; equal mean squares go to the lower channel.  order: host,
- * d int32 (output).  Returns TQ_OK or TQ_ERR_INVALID_ARG.  Host only. */
+ * d int32 (output).  Returns TQ_OK, or TQ_ERR_INVALID_ARG (null pointer,
+ * n_rows < 1, d_hi outside 0..d, or an inf / NaN in x).  Host only. */
 int tq_outlier_order(const float* x, int64_t n_rows, int d, int d_hi, int32_t* order);
 
 /* Encode rows of hi.d + lo.d elements, in place of two copies of the

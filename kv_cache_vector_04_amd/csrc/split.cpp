@@ -9,6 +9,7 @@
 // K, V and the queries, so that the split codec's hi half sees them.
 
 #include <algorithm>
+#include <cmath>
 #include <cstdint>
 #include <numeric>
 #include <vector>
@@ -24,6 +25,9 @@ extern "C" int tq_outlier_order(const float* x, int64_t n_rows, int d, int d_hi,
       const double v = x[r * d + c];
       ms[c] += v * v;
     }
+  // an inf or NaN sample has no defined order (and would break the sort)
+  for (int c = 0; c < d; ++c)
+    if (!std::isfinite(ms[c])) return TQ_ERR_INVALID_ARG;
   std::vector<int32_t> idx(d);
   std::iota(idx.begin(), idx.end(), 0);
   // larger mean square first; equal ones keep ascending channel order

@@ -341,3 +341,33 @@ def test_missing_library_fails_loudly(monkeypatch):
         tq.lib()
     with pytest.raises(ImportError):
         tq.build_codebook(128, 3)
+
+
+def test_outlier_order_matches_oracle_and_rejects_bad_input(L):
+    """The library's host channel order equals the oracle's permutation
+    (planted outlier channels, a tie broken to the lower channel), and
+    invalid or non-finite calibration rows return TQ_ERR_INVALID_ARG."""
+    import kv_cache_vector_04_amd as tq
+    from oracle import split as SP
+    rng = np.random.default_rng(21)
+    x = rng.standard_t(3, (2048, 128)).astype(np.float32)
+    x[:, [5, 77, 100]] *= 30.0
+    x[:, 9] = x[:, 8]                      # equal mean squares: channel 8 first
+    for d_hi in (0, 1, 9, 64, 128):
+        assert tq.outlier_order(x, d_hi).tolist() == SP.outlier_permutation(x.astype(np.float64), d_hi).tolist()
+    scale = np.array([1.0, 5.0, 5.0, 0.1, 3.0, 3.0], dtype=np.float32)
+    assert tq.outlier_order(np.tile(scale, (4, 1)), 3).tolist() == [1, 2, 4, 0, 3, 5]
+    order = np.empty(128, dtype=np.int32)
+
+    def call(arr, n, d, d_hi):
+        a = np.ascontiguousarray(arr, dtype=np.float32)
+        return L.tq_outlier_order(a.ctypes.data_as(ctypes.c_void_p), n, d, d_hi,
+                                  order.ctypes.data_as(ctypes.c_void_p))
+    assert call(x, 2048, 128, 64) == 0
+    for bad in (np.nan, np.inf):
+        y = x.copy()
+        y[3, 40] = bad
+        assert call(y, 2048, 128, 64) == -1
+    assert call(x, 0, 128, 64) == -1
+    assert call(x, 2048, 128, 129) == -1
+    assert call(x, 2048, 128, -1) == -1
