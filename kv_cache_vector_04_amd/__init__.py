@@ -11,6 +11,7 @@ import this module fail, rather than skip, when it is missing.
 """
 
 import ctypes
+import functools
 import os
 
 import numpy as np
@@ -159,6 +160,20 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
 
+def _on_stream(fn):
+    """A call given an explicit stream allocates its outputs and temporaries
+    on that stream, so the caching allocator keeps them until the stream's
+    work is done (a temporary freed on another stream could be reused while
+    the kernels still read it)."""
+    @functools.wraps(fn)
+    def wrapper(*args, stream=None, **kwargs):
+        if stream is None:
+            return fn(*args, **kwargs)
+        with torch.cuda.stream(stream):
+            return fn(*args, stream=stream, **kwargs)
+    return wrapper
+
+
 def _stream(stream=None):
     s = stream if stream is not None else torch.cuda.current_stream()
     return ctypes.c_void_p(s.cuda_stream)
@@ -236,6 +251,7 @@ def encode_workspace_bytes(kcodec, vcodec, n):
                                             int(n)))
 
 
+@_on_stream
 def encode_kv(kcodec, vcodec, k, v, rope=None, kout=None, vout=None, workspace=None,
               stream=None):
     """Encode rows of k with kcodec and rows of v with vcodec (either side may
@@ -324,6 +340,7 @@ class VQCodec:
         return self.d // 2 * self.block_bits // 8
 
 
+@_on_stream
 def encode_vq(codec, x, idx=None, norm=None, stream=None):
     """x: device [n, d] fp16/fp32 -> (idx [n, row_bytes] uint8, norm [n] fp32)."""
     _device_tensor(x, "x")
@@ -338,6 +355,7 @@ def encode_vq(codec, x, idx=None, norm=None, stream=None):
     return idx, norm
 
 
+@_on_stream
 def decode_vq(codec, idx, norm, n, dtype=None, out=None, stream=None):
     """Block codes back to vectors: out [n, d] (float16 unless dtype / out say float32)."""
     if out is None:
@@ -350,6 +368,7 @@ def decode_vq(codec, idx, norm, n, dtype=None, out=None, stream=None):
     return out
 
 
+@_on_stream
 def decode_kv(codec, pk, n, dtype=None, out=None, stream=None):
     """Packed rows back to vectors: returns out [n, d] (float16 unless dtype
     or out says float32)."""
@@ -402,6 +421,7 @@ class SplitPacked:
         self.structs = (TQPacked * 2)(self.hi.struct, self.lo.struct)
 
 
+@_on_stream
 def encode_split(kcodec, vcodec, k, v, kout=None, vout=None, stream=None):
     """Encode [..., 128] rows of k with the split codec kcodec and of v with
     vcodec (either may be None).  Returns (kout, vout) SplitPacked."""
@@ -434,6 +454,7 @@ def encode_split(kcodec, vcodec, k, v, kout=None, vout=None, stream=None):
     return kout, vout
 
 
+@_on_stream
 def decode_split(codec, pk, n, dtype=None, out=None, stream=None):
     """Both halves back to [n, 128] rows (float16 unless dtype / out say float32)."""
     if out is None:
@@ -448,6 +469,7 @@ def decode_split(codec, pk, n, dtype=None, out=None, stream=None):
     return out
 
 
+@_on_stream
 def attend_split(kcodec, vcodec, q, kpk, vpk, ctx, hkv, scale=0.0, out=None, scores_out=None,
                  workspace=None, stream=None):
     """Attention of q [batch, hq, n_q, 128] over split codes (SplitPacked with
@@ -474,6 +496,7 @@ def attend_workspace_bytes(batch, n_q, hq, hkv, ctx, d):
     return int(lib().tq_attend_decode_workspace(batch, n_q, hq, hkv, ctx, d))
 
 
+@_on_stream
 def attend_decode(kcodec, vcodec, q, kpk, vpk, ctx, hkv, scale=0.0, rope=None, out=None,
                   want_scores=False, workspace=None, stream=None):
     """Attention from codes.  q: device [batch, hq, n_q, d] fp16/fp32; kpk,
@@ -504,6 +527,7 @@ def inner_product_workspace_bytes(n_q, n, d, top_k):
     return int(lib().tq_inner_product_workspace(n_q, n, d, top_k))
 
 
+@_on_stream
 def inner_product(codec, q, pk, n, top_k=0, want_matrix=True, workspace=None, stream=None,
                   out_ids=None, out_vals=None):
     """Estimated inner products of q [n_q, d] against n packed rows.  Returns
