@@ -33,12 +33,60 @@ import numpy as np
 
 HBM_PEAK_GBS = 8000.0
 
-# HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE passes of the
-# current kernels, scaled by the runtime copy kernel's reading on a known
-# 64 MiB copy (FETCH_SIZE x2.0, WRITE_SIZE x1.0); None where the kernel has
-# changed since the counters were taken.
-TRAFFIC = {"encode": (65961 * 2 + 35840) * 1024,
-           "attend": (18329 * 2 + 520 + 369 * 2 + 16) * 1024}
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "kv_cache_vector_04_amd", "csrc")
+# rocprofv3 FETCH_SIZE / WRITE_SIZE summary of the bench's kernels: its
+# "per-launch:" lines give HBM bytes per launch (already scaled by the copy
+# kernel calibration) and the hash of each kernel source they were taken on.
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "gqa_decode_step_hbm_traffic.md")
+
+
+def source_hash(name):
+    import hashlib
+    with open(os.path.join(CSRC, name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def counter_traffic(part):
+    """HBM bytes per launch of `part` ("encode" or "attend") as the committed
+    counter summary records them, or None when that summary was taken on
+    other kernel sources than the ones built here (the kernel has changed
+    since the counters were taken) or has no such line."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            lines = f.read().splitlines()
+    except OSError:
+        return None
+    for line in lines:
+        f = line.split()
+        if len(f) >= 4 and f[0] == "per-launch:" and f[1] == part:
+            for src in f[3:]:
+                name, _, h = src.partition("@")
+                if not os.path.exists(os.path.join(CSRC, name)) or source_hash(name) != h:
+                    return None
+            return int(f[2])
+    return None
+
+
+def copy_bandwidth(torch, dev, nbytes=1 << 30, reps=10):
+    """Device-to-device copy of a 1 GiB buffer (torch's copy kernel), timed
+    with HIP events on the current stream: read + write bytes per second.
+    Context for the HBM-bound kernels (the practical ceiling of a plain
+    stream), not a peak."""
+    a = torch.ones((nbytes // 4,), dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    dt = e0.elapsed_time(e1) * 1e-3 / reps
+    del a, b
+    return 2.0 * nbytes / dt / 1e9
 
 
 def parse():
@@ -243,7 +291,7 @@ def main():
     roof = {"kernel": {"encode": "encode_kv_half_kernel<128,3,4> (keys prod + values mse, fp16)",
                        "attend": "decode_kernel<128,3,4> + merge_kernel<128>"}[dom],
             "bound": "hbm", "achieved": b_dom / t_dom / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": b_dom / t_dom / 1e9 / HBM_PEAK_GBS, "traffic": TRAFFIC.get(dom)}
+            "frac": b_dom / t_dom / 1e9 / HBM_PEAK_GBS, "traffic": counter_traffic(dom)}
 
     res = {
         "metric": "KV vectors encoded/s and decode-attention GB/s over packed codes (% of HBM peak)",
@@ -257,9 +305,15 @@ def main():
                    "vectors_per_step": vectors, "code_bytes_read_per_step": abytes,
                    "rotating_sets": S},
         "encode": enc, "attend": att, "two_pass_attention": two, "roofline": roof,
+        "context": {"hbm_copy_GB_per_s": copy_bandwidth(torch, dev),
+                    "note": "1 GiB device-to-device copy on this GPU (read + write bytes), "
+                            "the practical ceiling of a plain stream; peak stays 8 TB/s"},
     }
     if not a.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w)
+        res["cpu_baseline"], orc = cpu_baseline(w)
+        # agreement of this run's codes (buffer set 0) with the oracle's
+        # encode of the same input, taken in the same run
+        res["parity"] = oracle_agreement(w, orc, kpk[0], vpk[0], kc, vc)
     print(json.dumps(res), flush=True)
 
 
@@ -368,7 +422,60 @@ def bench_layers(a, torch, synth, tq, dev):
     if a.workload == "esm2":
         pairs = batch * heads * ctx * ctx
         res["attend"]["qk_pairs_per_s"] = pairs / ta
+    if not a.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_layers(a.workload, P, layers[0], d, ctx, heads)
     print(json.dumps(res), flush=True)
+
+
+def cpu_baseline_layers(workload, P, lay, d, ctx, heads):
+    """The fp64 numpy oracle on a bounded sample of a many-layer workload,
+    timed on this host with the BLAS pool at every core of this process:
+    llama_prefill: layer 0, KV heads 0-1 over all 131072 tokens (encode of
+    their keys and values, then the decode step of their 8 query heads);
+    esm2: layer 0, sequence 0 (RoPE and encode of the 20 heads' 1024 keys and
+    values, then all 1024 x 1024 scores and outputs of every head).  Rates
+    use the GPU's byte accounting."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    cb = 2
+    kc, kt = oracle.codebook(d, cb)
+    vc, vt = oracle.codebook(d, 3)
+    S = P["codec"].S.astype(np.float64)
+    flip = P["codec"].flip
+    if workload == "llama_prefill":
+        nh, nq = 2, 1
+        k = lay["k"][:nh].cpu().numpy().astype(np.float64)           # [2, ctx, d]
+        v = lay["v"][:nh].cpu().numpy().astype(np.float64)
+        q = lay["q"][:4 * nh].cpu().numpy().astype(np.float64).reshape(1, 4 * nh, 1, d)
+        sample = ("layer 0, KV heads 0-1 x 131072 tokens: encode of 262144 keys + 262144 values, "
+                  "then the decode step of their 8 query heads (fp64 numpy)")
+    else:
+        nh, nq = heads, ctx
+        k = lay["k"][0].cpu().numpy().astype(np.float64)              # [20, 1024, 64]
+        v = lay["v"][0].cpu().numpy().astype(np.float64)
+        q = lay["q"][:1].cpu().numpy().astype(np.float64)             # [1, 20, 1024, 64]
+        sample = ("layer 0, sequence 0: RoPE + encode of 20 x 1024 keys and values, then the "
+                  "bidirectional attention of the 20 heads (1024 x 1024 scores each; fp64 numpy)")
+    cores = _cores()
+    with threadpool_limits(limits=cores):
+        t0 = time.perf_counter()
+        if workload == "esm2":
+            pos = np.arange(ctx)
+            k = oracle.rope_interleaved(k, pos)
+            q = oracle.rope_interleaved(q, pos)
+        ek = oracle.encode_prod(k.reshape(-1, d), flip, kc, kt, S, keep_z=False)
+        ev = oracle.encode_mse(v.reshape(-1, d), flip, vt, keep_z=False)
+        kcodes = {"idx": ek.idx.reshape(1, nh, ctx, d), "sign": ek.sign.reshape(1, nh, ctx, d),
+                  "norm": ek.norm.reshape(1, nh, ctx), "rnorm": ek.rnorm.reshape(1, nh, ctx)}
+        vcodes = {"idx": ev.idx.reshape(1, nh, ctx, d), "norm": ev.norm.reshape(1, nh, ctx)}
+        oracle.attention_from_codes(q, kcodes, vcodes, {"signs": flip, "centroids": kc, "S": S},
+                                    {"signs": flip, "centroids": vc})
+        dt = time.perf_counter() - t0
+    n = nh * ctx
+    kout, vout = d * cb // 8 + d // 8 + 8, d * 3 // 8 + 4
+    nbytes = n * (2 * d + kout) + n * (2 * d + vout) + n * (kout + vout)
+    return {"value": 2 * n / dt, "unit": "vectors/s", "cores": int(cores), "kind": "oracle",
+            "seconds": dt, "GB_per_s": nbytes / dt / 1e9, "sample": sample}
 
 
 MFMA_F16_PEAK_TFLOPS = 2500.0
@@ -836,13 +943,19 @@ def _threads():
         return int(os.cpu_count())
 
 
-def cpu_baseline(w):
-    """The fp64 numpy oracle on a bounded sample of the same workload: encode
-    of KV heads 0..H-1 (all 32768 tokens, K prod b=4 and V mse b=4) and the
-    attention of their query heads, timed on this host."""
+def _cores():
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count()
+
+
+def _gqa_oracle_step(w, heads):
+    """The oracle's whole step on KV heads 0..heads-1: encode of their keys
+    (prod b=4) and values (mse b=4) over all 32768 tokens, then the attention
+    of their 4 query heads each."""
     import oracle
     d, ctx = 128, 32768
-    heads = 8
     kc, kt = oracle.codebook(d, 3)
     vc, vt = oracle.codebook(d, 4)
     S = w["codec"].S.astype(np.float64)
@@ -850,33 +963,84 @@ def cpu_baseline(w):
     k = w["k"][:heads].reshape(-1, d).astype(np.float64)
     v = w["v"][:heads].reshape(-1, d).astype(np.float64)
     q = w["q"][:4 * heads].astype(np.float64).reshape(1, 4 * heads, 1, d)
+    t0 = time.perf_counter()
+    ek = oracle.encode_prod(k, flip, kc, kt, S)
+    ev = oracle.encode_mse(v, flip, vt)
+    kcodes = {"idx": ek.idx.reshape(1, heads, ctx, d), "sign": ek.sign.reshape(1, heads, ctx, d),
+              "norm": ek.norm.reshape(1, heads, ctx), "rnorm": ek.rnorm.reshape(1, heads, ctx)}
+    vcodes = {"idx": ev.idx.reshape(1, heads, ctx, d), "norm": ev.norm.reshape(1, heads, ctx)}
+    oracle.attention_from_codes(q, kcodes, vcodes, {"signs": flip, "centroids": kc, "S": S},
+                                {"signs": flip, "centroids": vc})
+    return time.perf_counter() - t0, ek, ev
+
+
+def cpu_baseline(w):
+    """The fp64 numpy oracle on a bounded sample of the same workload, timed
+    on this host: the whole step (8 KV heads) with the BLAS pool at every
+    core of this process (median of 3), and one KV head with one thread.
+    Bytes are counted as for the GPU: 256 + 72 B per key and 256 + 68 B per
+    value encoded, 140 B of codes per token and KV head attended.  Returns
+    (baseline record, the oracle's codes of the full step)."""
+    from threadpoolctl import threadpool_limits
+    ctx = 32768
+    per_head = ctx * ((256 + 72) + (256 + 68) + 140)
+    cores = _cores()
     times = []
-    for _ in range(3):
-        t0 = time.perf_counter()
-        ek = oracle.encode_prod(k, flip, kc, kt, S)
-        ev = oracle.encode_mse(v, flip, vt)
-        kcodes = {"idx": ek.idx.reshape(1, heads, ctx, d), "sign": ek.sign.reshape(1, heads, ctx, d),
-                  "norm": ek.norm.reshape(1, heads, ctx), "rnorm": ek.rnorm.reshape(1, heads, ctx)}
-        vcodes = {"idx": ev.idx.reshape(1, heads, ctx, d), "norm": ev.norm.reshape(1, heads, ctx)}
-        oracle.attention_from_codes(q, kcodes, vcodes, {"signs": flip, "centroids": kc, "S": S},
-                                    {"signs": flip, "centroids": vc})
-        times.append(time.perf_counter() - t0)
+    with threadpool_limits(limits=cores):
+        for _ in range(3):
+            dt, ek, ev = _gqa_oracle_step(w, 8)
+            times.append(dt)
     dt = float(np.median(times))
-    try:
-        cores = len(os.sched_getaffinity(0))
-    except AttributeError:
-        cores = os.cpu_count()
-    threads = None
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
-    except Exception:
-        threads = cores
-    return {"value": 2 * heads * ctx / dt, "unit": "vectors/s", "cores": int(threads),
-            "kind": "oracle", "seconds": dt,
-            "sample": "one full step (%d KV heads): encode of %d keys + %d values and the "
-                      "attention of %d query heads over 32768 tokens (fp64 numpy), median of 3" %
-                      (heads, heads * ctx, heads * ctx, 4 * heads)}
+    with threadpool_limits(limits=1):
+        dt1, _, _ = _gqa_oracle_step(w, 1)
+    rec = {"value": 2 * 8 * ctx / dt, "unit": "vectors/s", "cores": int(cores), "kind": "oracle",
+           "seconds": dt, "GB_per_s": 8 * per_head / dt / 1e9,
+           "single_thread": {"value": 2 * ctx / dt1, "unit": "vectors/s", "cores": 1,
+                             "seconds": dt1, "GB_per_s": per_head / dt1 / 1e9,
+                             "sample": "one KV head: encode of 32768 keys + 32768 values and the "
+                                       "attention of its 4 query heads (fp64 numpy, BLAS at 1 "
+                                       "thread)"},
+           "sample": "one full step (8 KV heads): encode of 262144 keys + 262144 values and the "
+                     "attention of 32 query heads over 32768 tokens (fp64 numpy, BLAS at %d "
+                     "threads), median of 3" % cores}
+    return rec, (ek, ev)
+
+
+def oracle_agreement(w, orc, kpk, vpk, kc, vc):
+    """Code agreement between the GPU's packed keys and values (one buffer
+    set of this run) and the oracle's encode of the same input: mismatch
+    fractions of the codes, the fraction of coordinates whose fp64 rotated
+    value lies within 1e-5 of a threshold (a property of the data), and the
+    QJL sign bits against [S r >= 0] recomputed in fp64 from the GPU's own
+    codes.  Every mismatch must lie inside the 1e-5 band."""
+    import oracle
+    ek, ev = orc
+    d, band = 128, 1e-5
+    kcb, kt = oracle.codebook(d, 3)
+    _, vt = oracle.codebook(d, 4)
+    S = w["codec"].S.astype(np.float64)
+    host = lambda t: t.detach().cpu().numpy()
+    out = {}
+    for name, enc, pk, cb, t in (("K", ek, kpk, 3, kt), ("V", ev, vpk, 4, vt)):
+        g = oracle.unpack_codes(host(pk.idx), d, cb)
+        bad = g != enc.idx
+        near = np.zeros(enc.z.shape, dtype=bool)
+        for a in range(0, enc.z.shape[0], 16384):
+            zz = enc.z[a:a + 16384]
+            near[a:a + 16384] = np.min(np.abs(zz[..., None] - t), axis=-1) <= band
+        out[name] = {"code_mismatch_frac": float(bad.mean()),
+                     "mismatch_outside_band": int((bad & ~near).sum()),
+                     "near_band_frac": float(near.mean()),
+                     "rows_with_a_mismatch_frac": float(bad.any(axis=1).mean())}
+        if name == "K":
+            sign = oracle.unpack_bits(host(pk.qjl), d)
+            p = oracle.qjl_projection(oracle.codec.residual_from_codes(enc.z, g, kcb), S)
+            sb = sign != (p >= 0)
+            out[name]["qjl_mismatch_frac"] = float(sb.mean())
+            out[name]["qjl_mismatch_outside_band"] = int((sb & (np.abs(p) > band)).sum())
+    out["note"] = ("GPU codes of one buffer set vs the fp64 oracle's encode of the same input; "
+                   "rule: mismatches only within 1e-5 of a threshold, at most 1e-4 of codes")
+    return out
 
 
 if __name__ == "__main__":

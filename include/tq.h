@@ -137,8 +137,9 @@ typedef struct tq_rope {
  * (RoPE on K if `rope` is not NULL), nu = |x|, z = Pi x / nu, idx_i =
  * #{k : z_i >= t_k}, and for TQ_PROD r = z - c[idx], gamma = |r|, signs of
  * S r ("FibQuant" 2.3; "Google presenta TurboQuant" mechanics and prod
- * sections).  The zero vector, and a vector with a non-finite element,
- * encode as z = 0 with nu = 0.
+ * sections).  The zero vector encodes as z = 0 with nu = 0.  A vector with
+ * an inf or NaN element (after RoPE, when applied) also encodes as z = 0 and
+ * stores its non-finite norm: inf, or NaN when a NaN is present.
  *   k, v      device, n_rows x d elements of type `dtype`, 16-byte aligned
  *   kc, vc    host structs (kc TQ_PROD or TQ_MSE; vc either); d = 64, 128 or
  *             1536 (d = 1536: Pi uses H_12 (x) H_128, H_12 by Paley's
@@ -312,8 +313,11 @@ int tq_decode_vq(const tq_vq_codec* c, const uint8_t* idx, const float* norm, in
  *   scale  0 selects 1/sqrt(d)
  *   out device [batch][hq][n_q][d] fp32
  *   scores_out  NULL, or device [batch][hq][n_q][ctx] fp32 receiving s_j
- *   workspace   device, >= tq_attend_decode_workspace(...) bytes, zero-filled
- *               before its first use; each call leaves it ready for the next.
+ *   workspace   device, >= tq_attend_decode_workspace(...) bytes, 16-byte
+ *               aligned; it receives the per-token-range partial results
+ *               (max, sum, weighted value sum per query row) that the merge
+ *               reads back.  Every entry read is written first by the same
+ *               call, so its contents need no initialisation.
  * Calls that share one workspace must not overlap in time. */
 size_t tq_attend_decode_workspace(int batch, int n_q, int hq, int hkv,
                                   int64_t ctx, int d);

@@ -12,6 +12,7 @@ import this module fail, rather than skip, when it is missing.
 
 import ctypes
 import functools
+import inspect
 import os
 
 import numpy as np
@@ -164,7 +165,11 @@ def _on_stream(fn):
     """A call given an explicit stream allocates its outputs and temporaries
     on that stream, so the caching allocator keeps them until the stream's
     work is done (a temporary freed on another stream could be reused while
-    the kernels still read it)."""
+    the kernels still read it).  `stream` is keyword-only in every wrapped
+    call, so it cannot arrive positionally and bypass this."""
+    if inspect.signature(fn).parameters["stream"].kind is not inspect.Parameter.KEYWORD_ONLY:
+        raise TypeError("%s: stream must be keyword-only" % fn.__name__)
+
     @functools.wraps(fn)
     def wrapper(*args, stream=None, **kwargs):
         if stream is None:
@@ -193,6 +198,67 @@ def _device_tensor(t, name):
     if not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
     return t
+
+
+def _out_tensor(t, name, shape, dtype):
+    """A caller-given output buffer: CUDA, contiguous, of exactly `shape`
+    and `dtype` (the kernels write that many elements through its pointer)."""
+    _device_tensor(t, name)
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError("%s must be a %s tensor of shape %s, got %s %s"
+                         % (name, dtype, tuple(shape), t.dtype, tuple(t.shape)))
+    return t
+
+
+def _workspace(t, need, device):
+    """The caller's workspace (CUDA uint8, at least `need` bytes), or a new
+    one.  The kernels write every byte they read back, so it is not cleared."""
+    if t is None:
+        return torch.empty((max(need, 16),), dtype=torch.uint8, device=device)
+    _device_tensor(t, "workspace")
+    if t.numel() * t.element_size() < need:
+        raise ValueError("workspace holds %d bytes, the call needs %d"
+                         % (t.numel() * t.element_size(), need))
+    return t
+
+
+def _check_packed(pk, codec, n, name):
+    """pk must be a Packed laid out for `codec` and hold at least n rows:
+    the C ABI's tq_packed carries no row count, so this is the only place an
+    undersized or mismatched buffer can be caught before a kernel runs."""
+    if not isinstance(pk, Packed):
+        raise ValueError("%s must be a Packed" % name)
+    if pk.n < n:
+        raise ValueError("%s holds %d rows, the call reads or writes %d" % (name, pk.n, n))
+    row = codec.d * codec.code_bits // 8
+    if pk.idx.dim() != 2 or pk.idx.shape[1] != row or pk.idx.dtype != torch.uint8:
+        raise ValueError("%s.idx rows are not %d bytes (codec d=%d, %d-bit codes)"
+                         % (name, row, codec.d, codec.code_bits))
+    if (pk.qjl is None) != (codec.mode != TQ_PROD):
+        raise ValueError("%s planes do not match the codec's mode" % name)
+    planes = [("idx", pk.idx), ("norm", pk.norm)]
+    if codec.mode == TQ_PROD:
+        if pk.qjl.dim() != 2 or pk.qjl.shape[1] != codec.m // 8:
+            raise ValueError("%s.qjl rows are not %d bytes" % (name, codec.m // 8))
+        planes += [("qjl", pk.qjl), ("rnorm", pk.rnorm)]
+    for what, t in planes:
+        _device_tensor(t, "%s.%s" % (name, what))
+        if t.shape[0] < pk.n:
+            raise ValueError("%s.%s holds fewer than %d rows" % (name, what, pk.n))
+
+
+def _check_split_packed(pk, codec, n, name):
+    if not isinstance(pk, SplitPacked):
+        raise ValueError("%s must be a SplitPacked" % name)
+    _check_packed(pk.hi, codec.hi, n, name + ".hi")
+    _check_packed(pk.lo, codec.lo, n, name + ".lo")
+
+
+def _check_heads(hq, hkv, ctx):
+    if hkv <= 0 or hq <= 0 or hq % hkv:
+        raise ValueError("hq = %d must be a positive multiple of hkv = %d" % (hq, hkv))
+    if ctx <= 0:
+        raise ValueError("ctx must be positive")
 
 
 class Codec:
@@ -252,7 +318,7 @@ def encode_workspace_bytes(kcodec, vcodec, n):
 
 
 @_on_stream
-def encode_kv(kcodec, vcodec, k, v, rope=None, kout=None, vout=None, workspace=None,
+def encode_kv(kcodec, vcodec, k, v, rope=None, kout=None, vout=None, workspace=None, *,
               stream=None):
     """Encode rows of k with kcodec and rows of v with vcodec (either side may
     be None).  k / v: device tensors [..., d], fp16 or fp32.  rope: None or
@@ -274,17 +340,23 @@ def encode_kv(kcodec, vcodec, k, v, rope=None, kout=None, vout=None, workspace=N
         dt = d2 if dt is None else dt
         if d2 != dt:
             raise ValueError("k and v must share a dtype")
+    if n is None:
+        raise ValueError("encode_kv needs at least one codec")
     dev = (k if kcodec is not None else v).device
-    if kcodec is not None and kout is None:
-        kout = Packed(kcodec, n, dev)
-    if vcodec is not None and vout is None:
-        vout = Packed(vcodec, n, dev)
+    if kcodec is not None:
+        if kout is None:
+            kout = Packed(kcodec, n, dev)
+        _check_packed(kout, kcodec, n, "kout")
+    if vcodec is not None:
+        if vout is None:
+            vout = Packed(vcodec, n, dev)
+        _check_packed(vout, vcodec, n, "vout")
     r = None
     if rope is not None:
         r = TQRope(float(rope[0]), 0, int(rope[1]))
     need = encode_workspace_bytes(kcodec, vcodec, n)
-    if workspace is None and need > 0:
-        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+    if workspace is not None or need > 0:
+        workspace = _workspace(workspace, need, dev)
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = lib().tq_encode_kv(ctypes.byref(kcodec.struct) if kcodec else None,
                             ctypes.byref(vcodec.struct) if vcodec else None,
@@ -341,14 +413,18 @@ class VQCodec:
 
 
 @_on_stream
-def encode_vq(codec, x, idx=None, norm=None, stream=None):
+def encode_vq(codec, x, idx=None, norm=None, *, stream=None):
     """x: device [n, d] fp16/fp32 -> (idx [n, row_bytes] uint8, norm [n] fp32)."""
     _device_tensor(x, "x")
+    if x.shape[-1] != codec.d:
+        raise ValueError("last dimension must be d=%d" % codec.d)
     n = x.numel() // codec.d
     if idx is None:
         idx = torch.empty((n, codec.row_bytes), dtype=torch.uint8, device=x.device)
     if norm is None:
         norm = torch.empty((n,), dtype=torch.float32, device=x.device)
+    _out_tensor(idx, "idx", (n, codec.row_bytes), torch.uint8)
+    _out_tensor(norm, "norm", (n,), torch.float32)
     st = lib().tq_encode_vq(ctypes.byref(codec.struct), _ptr(x), _dtype_code(x), n, _ptr(idx),
                             _ptr(norm), _stream(stream))
     _check(st, "tq_encode_vq")
@@ -356,12 +432,19 @@ def encode_vq(codec, x, idx=None, norm=None, stream=None):
 
 
 @_on_stream
-def decode_vq(codec, idx, norm, n, dtype=None, out=None, stream=None):
+def decode_vq(codec, idx, norm, n, dtype=None, out=None, *, stream=None):
     """Block codes back to vectors: out [n, d] (float16 unless dtype / out say float32)."""
+    _device_tensor(idx, "idx")
+    _device_tensor(norm, "norm")
+    if idx.dim() != 2 or idx.shape[0] < n or idx.shape[1] != codec.row_bytes or norm.numel() < n \
+            or idx.dtype != torch.uint8 or norm.dtype != torch.float32:
+        raise ValueError("idx must hold n x %d uint8 and norm n float32" % codec.row_bytes)
     if out is None:
         out = torch.empty((n, codec.d), dtype=dtype if dtype is not None else torch.float16,
                           device=idx.device)
     _device_tensor(out, "out")
+    if out.numel() != n * codec.d:
+        raise ValueError("out must hold n x d elements")
     st = lib().tq_decode_vq(ctypes.byref(codec.struct), _ptr(idx), _ptr(norm), int(n), _ptr(out),
                             _dtype_code(out), _stream(stream))
     _check(st, "tq_decode_vq")
@@ -369,9 +452,10 @@ def decode_vq(codec, idx, norm, n, dtype=None, out=None, stream=None):
 
 
 @_on_stream
-def decode_kv(codec, pk, n, dtype=None, out=None, stream=None):
+def decode_kv(codec, pk, n, dtype=None, out=None, *, stream=None):
     """Packed rows back to vectors: returns out [n, d] (float16 unless dtype
     or out says float32)."""
+    _check_packed(pk, codec, n, "pk")
     if out is None:
         dt = dtype if dtype is not None else torch.float16
         out = torch.empty((n, codec.d), dtype=dt, device=pk.idx.device)
@@ -422,7 +506,7 @@ class SplitPacked:
 
 
 @_on_stream
-def encode_split(kcodec, vcodec, k, v, kout=None, vout=None, stream=None):
+def encode_split(kcodec, vcodec, k, v, kout=None, vout=None, *, stream=None):
     """Encode [..., 128] rows of k with the split codec kcodec and of v with
     vcodec (either may be None).  Returns (kout, vout) SplitPacked."""
     n = dt = None
@@ -440,11 +524,17 @@ def encode_split(kcodec, vcodec, k, v, kout=None, vout=None, stream=None):
         dt = d2 if dt is None else dt
         if d2 != dt:
             raise ValueError("k and v must share a dtype")
+    if n is None:
+        raise ValueError("encode_split needs at least one codec")
     dev = (k if kcodec is not None else v).device
-    if kcodec is not None and kout is None:
-        kout = SplitPacked(kcodec, n, dev)
-    if vcodec is not None and vout is None:
-        vout = SplitPacked(vcodec, n, dev)
+    if kcodec is not None:
+        if kout is None:
+            kout = SplitPacked(kcodec, n, dev)
+        _check_split_packed(kout, kcodec, n, "kout")
+    if vcodec is not None:
+        if vout is None:
+            vout = SplitPacked(vcodec, n, dev)
+        _check_split_packed(vout, vcodec, n, "vout")
     st = lib().tq_encode_split(ctypes.byref(kcodec.struct) if kcodec else None,
                                ctypes.byref(vcodec.struct) if vcodec else None,
                                _ptr(k) if kcodec else None, _ptr(v) if vcodec else None, dt, n,
@@ -455,8 +545,9 @@ def encode_split(kcodec, vcodec, k, v, kout=None, vout=None, stream=None):
 
 
 @_on_stream
-def decode_split(codec, pk, n, dtype=None, out=None, stream=None):
+def decode_split(codec, pk, n, dtype=None, out=None, *, stream=None):
     """Both halves back to [n, 128] rows (float16 unless dtype / out say float32)."""
+    _check_split_packed(pk, codec, n, "pk")
     if out is None:
         dt = dtype if dtype is not None else torch.float16
         out = torch.empty((n, 128), dtype=dt, device=pk.hi.idx.device)
@@ -471,18 +562,24 @@ def decode_split(codec, pk, n, dtype=None, out=None, stream=None):
 
 @_on_stream
 def attend_split(kcodec, vcodec, q, kpk, vpk, ctx, hkv, scale=0.0, out=None, scores_out=None,
-                 workspace=None, stream=None):
+                 workspace=None, *, stream=None):
     """Attention of q [batch, hq, n_q, 128] over split codes (SplitPacked with
     rows [batch][hkv][ctx]); returns out [batch, hq, n_q, 128] fp32."""
     _device_tensor(q, "q")
+    if q.dim() != 4:
+        raise ValueError("q must be [batch, hq, n_q, 128]")
     batch, hq, n_q, d = q.shape
     if d != 128:
         raise ValueError("split attention takes 128 channels")
+    _check_heads(hq, hkv, ctx)
+    _check_split_packed(kpk, kcodec, batch * hkv * ctx, "kpk")
+    _check_split_packed(vpk, vcodec, batch * hkv * ctx, "vpk")
     if out is None:
         out = torch.empty((batch, hq, n_q, d), dtype=torch.float32, device=q.device)
-    if workspace is None:
-        need = attend_workspace_bytes(batch, n_q, hq, hkv, ctx, d)
-        workspace = torch.zeros((max(need, 1),), dtype=torch.uint8, device=q.device)
+    _out_tensor(out, "out", (batch, hq, n_q, d), torch.float32)
+    if scores_out is not None:
+        _out_tensor(scores_out, "scores_out", (batch, hq, n_q, ctx), torch.float32)
+    workspace = _workspace(workspace, attend_workspace_bytes(batch, n_q, hq, hkv, ctx, d), q.device)
     wbytes = workspace.numel() * workspace.element_size()
     st = lib().tq_attend_split(ctypes.byref(kcodec.struct), ctypes.byref(vcodec.struct), _ptr(q),
                                _dtype_code(q), batch, n_q, hq, hkv, kpk.structs, vpk.structs,
@@ -498,20 +595,26 @@ def attend_workspace_bytes(batch, n_q, hq, hkv, ctx, d):
 
 @_on_stream
 def attend_decode(kcodec, vcodec, q, kpk, vpk, ctx, hkv, scale=0.0, rope=None, out=None,
-                  want_scores=False, workspace=None, stream=None):
+                  want_scores=False, workspace=None, *, stream=None):
     """Attention from codes.  q: device [batch, hq, n_q, d] fp16/fp32; kpk,
     vpk: Packed rows [batch][hkv][ctx].  rope: None or (base, pos0).
     Returns out [batch, hq, n_q, d] fp32 (and scores [batch, hq, n_q, ctx])."""
     _device_tensor(q, "q")
+    if q.dim() != 4:
+        raise ValueError("q must be [batch, hq, n_q, d]")
     batch, hq, n_q, d = q.shape
+    if d != kcodec.d or d != vcodec.d:
+        raise ValueError("q rows hold %d elements, the codecs d = %d / %d" % (d, kcodec.d, vcodec.d))
+    _check_heads(hq, hkv, ctx)
+    _check_packed(kpk, kcodec, batch * hkv * ctx, "kpk")
+    _check_packed(vpk, vcodec, batch * hkv * ctx, "vpk")
     if out is None:
         out = torch.empty((batch, hq, n_q, d), dtype=torch.float32, device=q.device)
+    _out_tensor(out, "out", (batch, hq, n_q, d), torch.float32)
     scores = None
     if want_scores:
         scores = torch.empty((batch, hq, n_q, ctx), dtype=torch.float32, device=q.device)
-    need = attend_workspace_bytes(batch, n_q, hq, hkv, ctx, d)
-    if workspace is None:
-        workspace = torch.zeros((max(need, 16),), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, attend_workspace_bytes(batch, n_q, hq, hkv, ctx, d), q.device)
     r = TQRope(float(rope[0]), int(rope[1]), 0) if rope is not None else None
     st = lib().tq_attend_decode(ctypes.byref(kcodec.struct), ctypes.byref(vcodec.struct), _ptr(q),
                                 _dtype_code(q), batch, n_q, hq, hkv,
@@ -528,13 +631,16 @@ def inner_product_workspace_bytes(n_q, n, d, top_k):
 
 
 @_on_stream
-def inner_product(codec, q, pk, n, top_k=0, want_matrix=True, workspace=None, stream=None,
-                  out_ids=None, out_vals=None):
+def inner_product(codec, q, pk, n, top_k=0, want_matrix=True, workspace=None, out_ids=None,
+                  out_vals=None, *, stream=None):
     """Estimated inner products of q [n_q, d] against n packed rows.  Returns
     the [n_q, n] matrix (if want_matrix) and, for top_k > 0, (ids, scores)
     (written into out_ids / out_vals when given)."""
     _device_tensor(q, "q")
+    if q.dim() != 2 or q.shape[1] != codec.d:
+        raise ValueError("q must be [n_q, %d]" % codec.d)
     n_q, d = q.shape
+    _check_packed(pk, codec, n, "pk")
     out = torch.empty((n_q, n), dtype=torch.float32, device=q.device) if want_matrix else None
     ids = vals = None
     if top_k:
@@ -547,9 +653,7 @@ def inner_product(codec, q, pk, n, top_k=0, want_matrix=True, workspace=None, st
         if ids.shape != (n_q, top_k) or vals.shape != (n_q, top_k) or ids.dtype != torch.int64 \
                 or vals.dtype != torch.float32:
             raise ValueError("out_ids / out_vals must be [n_q, top_k] int64 / float32")
-    need = inner_product_workspace_bytes(n_q, n, d, top_k)
-    if workspace is None:
-        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, inner_product_workspace_bytes(n_q, n, d, top_k), q.device)
     st = lib().tq_inner_product(ctypes.byref(codec.struct), _ptr(q), _dtype_code(q), n_q,
                                 ctypes.byref(pk.struct), int(n), _ptr(out), int(top_k), _ptr(ids),
                                 _ptr(vals), _ptr(workspace),

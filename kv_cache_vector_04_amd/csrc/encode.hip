@@ -233,10 +233,17 @@ __global__ __launch_bounds__(kEncWaves * kWave) void encode_kernel(EncodeParams 
       // two that brings its largest entry into [0.5, 1).
       float nu2 = sum_squares<D>(x);
       if (!(nu2 >= 0x1p-100f && nu2 <= 0x1p100f)) {
+        // a NaN element makes the sum NaN (fmaxf below would skip it)
+        const bool has_nan = !(nu2 == nu2);
         float mx = 0.f;
 #pragma unroll
         for (int i = 0; i < D; ++i) mx = fmaxf(mx, fabsf(x[i]));
-        if (mx > 0.f && mx <= 3.4e38f) {
+        if (has_nan || !(mx <= 3.4e38f)) {
+          // a non-finite input encodes as the zero vector; nu2 stays inf or
+          // NaN, and so does the stored norm
+#pragma unroll
+          for (int i = 0; i < D; ++i) x[i] = 0.f;
+        } else if (mx > 0.f) {
           int e;
           frexpf(mx, &e);
           const float sc = ldexpf(1.f, -e);
@@ -244,10 +251,6 @@ __global__ __launch_bounds__(kEncWaves * kWave) void encode_kernel(EncodeParams 
 #pragma unroll
           for (int i = 0; i < D; ++i) x[i] *= sc;
           nu2 = sum_squares<D>(x);
-        } else if (!(mx <= 3.4e38f)) {
-          // a non-finite input encodes as the zero vector
-#pragma unroll
-          for (int i = 0; i < D; ++i) x[i] = 0.f;
         }
       }
       nu_s = sqrtf(nu2);

@@ -129,16 +129,11 @@ __global__ __launch_bounds__(64 * kXWaves) void wide_transform_kernel(WideXParam
         x[a][1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u >> 16));
       }
     }
-    // a vector with a non-finite element encodes as the zero vector
     bool bad = false;
 #pragma unroll
     for (int a = 0; a < kWA; ++a) bad |= !__builtin_isfinite(x[a][0]) || !__builtin_isfinite(x[a][1]);
-    if (__ballot(bad) != 0ull) {
-#pragma unroll
-      for (int a = 0; a < kWA; ++a) x[a][0] = x[a][1] = 0.f;
-    }
-    float nu = 0.f;
-    if constexpr (MODE != kWQuery) {
+    const bool nonfinite = __ballot(bad) != 0ull;
+    auto sum_sq = [&]() {
       float t[kWA];
 #pragma unroll
       for (int a = 0; a < kWA; ++a) t[a] = fmaf(x[a][0], x[a][0], x[a][1] * x[a][1]);
@@ -146,7 +141,43 @@ __global__ __launch_bounds__(64 * kXWaves) void wide_transform_kernel(WideXParam
                  ((t[8] + t[9]) + (t[10] + t[11]));
 #pragma unroll
       for (int s = 32; s >= 1; s >>= 1) ss += __shfl_xor(ss, s);
-      nu = sqrtf(ss);
+      return ss;
+    };
+    float nu = 0.f, nu_x = 0.f;   // the stored norm; the norm of the row z is made from
+    if constexpr (MODE != kWQuery) {
+      // a non-finite row keeps its sum of squares (inf, or NaN when a NaN is
+      // present) as its stored norm
+      float ss = sum_sq();
+      float pre = 1.f;
+      if (!nonfinite && !(ss >= 0x1p-100f && ss <= 0x1p100f)) {
+        // squares outside the normal fp32 range (fp32 input only): scale the
+        // row exactly by the power of two that brings its largest entry into
+        // [0.5, 1), as the d <= 128 encoder does
+        float mx = 0.f;
+#pragma unroll
+        for (int a = 0; a < kWA; ++a) mx = fmaxf(mx, fmaxf(fabsf(x[a][0]), fabsf(x[a][1])));
+#pragma unroll
+        for (int s = 32; s >= 1; s >>= 1) mx = fmaxf(mx, __shfl_xor(mx, s));
+        if (mx > 0.f) {
+          int e;
+          frexpf(mx, &e);
+          const float sc = ldexpf(1.f, -e);
+          pre = ldexpf(1.f, e);
+#pragma unroll
+          for (int a = 0; a < kWA; ++a) {
+            x[a][0] *= sc;
+            x[a][1] *= sc;
+          }
+          ss = sum_sq();
+        }
+      }
+      nu_x = sqrtf(ss);
+      nu = nu_x * pre;
+    }
+    // a vector with a non-finite element encodes as the zero vector
+    if (nonfinite) {
+#pragma unroll
+      for (int a = 0; a < kWA; ++a) x[a][0] = x[a][1] = 0.f;
     }
     // D: sign flip of coordinate 128 a + 2 lane + e
 #pragma unroll
@@ -175,7 +206,7 @@ __global__ __launch_bounds__(64 * kXWaves) void wide_transform_kernel(WideXParam
         }
     }
     // H_12 across the chunks, then the scale
-    const float inv = MODE == kWQuery ? p.inv_sqrt_d : (nu > 0.f ? p.inv_sqrt_d / nu : 0.f);
+    const float inv = MODE == kWQuery ? p.inv_sqrt_d : (nu_x > 0.f ? p.inv_sqrt_d / nu_x : 0.f);
     float z[kWA][2];
 #pragma unroll
     for (int e = 0; e < 2; ++e)

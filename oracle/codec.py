@@ -25,7 +25,8 @@ Readings where the pages are silent:
 * A code is the number of thresholds at or below the coordinate,
   idx = #{k : z >= t_k} (a value on a threshold goes to the upper cell).
 * The zero vector encodes as u = 0: idx = #{k : 0 >= t_k}, r = -c[idx],
-  and its estimate is 0 because nu = 0.
+  and its estimate is 0 because nu = 0.  A row with an inf or NaN element
+  gets the same codes and keeps its non-finite norm.
 * Packing: a row's codes form one LSB-first bit stream, code i in stream
   bits [i b, (i+1) b), stream bit k = bit (k mod 8) of byte k // 8; a row
   occupies exactly d b / 8 bytes, row j at byte j d b / 8 (fixed rate, fixed
@@ -71,11 +72,17 @@ def _as_rows(x):
 
 
 def _normalize_rotate(x, signs):
-    """nu = |x| and z = Pi (x / nu), with u = 0 for the zero vector."""
-    nu = np.sqrt(np.sum(x * x, axis=1))
+    """nu = |x| and z = Pi (x / nu), with u = 0 for the zero vector.
+
+    A row holding an inf or NaN has no unit vector; the pages define no code
+    for it.  Here it also takes u = 0 (the zero vector's codes) and keeps its
+    non-finite norm: inf when its largest element is infinite, NaN when an
+    element is NaN (the sum of squares computed as written)."""
+    with np.errstate(over="ignore", invalid="ignore"):
+        nu = np.sqrt(np.sum(x * x, axis=1))
+    live = np.all(np.isfinite(x), axis=1) & (nu > 0)
     u = np.zeros_like(x)
-    nz = nu > 0
-    u[nz] = x[nz] / nu[nz, None]
+    u[live] = x[live] / nu[live, None]
     return nu, rotate(u, signs)
 
 

@@ -132,9 +132,14 @@ def code_bits(n_codes):
 def encode_vq(x, signs, code):
     """nu = |x|, z = Pi x / nu, idx_j = nearest codeword of (z_2j, z_2j+1)."""
     x = np.asarray(x, dtype=np.float64)
-    nu = np.linalg.norm(x, axis=1)
-    safe = np.where(nu > 0, nu, 1.0)
-    z = rotate(x / safe[:, None], signs) * (nu > 0)[:, None]
+    with np.errstate(over="ignore", invalid="ignore"):
+        nu = np.sqrt(np.sum(x * x, axis=1))
+    # the zero row, and a row with an inf or NaN element (which keeps its
+    # non-finite norm), take z = 0
+    live = np.all(np.isfinite(x), axis=1) & (nu > 0)
+    u = np.zeros_like(x)
+    u[live] = x[live] / nu[live, None]
+    z = rotate(u, signs)
     n, d = z.shape
     idx = nearest(z.reshape(-1, 2), code).reshape(n, d // 2)
     return idx, nu, z

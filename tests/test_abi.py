@@ -371,3 +371,19 @@ def test_outlier_order_matches_oracle_and_rejects_bad_input(L):
     assert call(x, 0, 128, 64) == -1
     assert call(x, 2048, 128, 129) == -1
     assert call(x, 2048, 128, -1) == -1
+
+
+def test_stream_is_keyword_only():
+    """A stream can only be passed by name, so every call routes it through
+    the wrapper that allocates outputs on that stream; a positional stream
+    is a TypeError raised before anything reaches the GPU."""
+    import inspect
+    kinds = {}
+    for fn in (tq.encode_kv, tq.encode_vq, tq.decode_vq, tq.decode_kv, tq.encode_split,
+               tq.decode_split, tq.attend_split, tq.attend_decode, tq.inner_product):
+        kinds[fn.__name__] = inspect.signature(fn.__wrapped__).parameters["stream"].kind
+    assert set(kinds.values()) == {inspect.Parameter.KEYWORD_ONLY}, kinds
+    with pytest.raises(TypeError):
+        tq.encode_kv(None, None, None, None, None, None, None, None, object())
+    with pytest.raises(TypeError):
+        tq.inner_product(None, None, None, 0, 0, True, None, None, None, object())

@@ -8,7 +8,7 @@ import torch
 
 import oracle
 import synth
-from parity import check_rows, gpu_codes, to_np
+from parity import check_rows, check_scores, gpu_codes, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -53,7 +53,7 @@ def _run(B, Hq, Hkv, ctx, nq, d, kbits, vbits, seed, dist="normal"):
     out, sc = tq.attend_decode(kc, vc, torch.from_numpy(q).cuda(), kpk, vpk, ctx, Hkv, want_scores=True)
     torch.cuda.synchronize()
     ref_out, ref_sc = _oracle_attention(q, kpk, vpk, kc, vc, draws, B, Hkv, ctx)
-    e1 = check_rows(to_np(sc), ref_sc)
+    e1 = check_scores(to_np(sc), ref_sc)
     e2 = check_rows(to_np(out), ref_out)
     return e1, e2
 
@@ -68,7 +68,7 @@ def test_attend_gqa_decode_full():
     out, sc = tq.attend_decode(kc, vc, torch.from_numpy(q).cuda(), kpk, vpk, 32768, 8, want_scores=True)
     torch.cuda.synchronize()
     ref_out, ref_sc = _oracle_attention(q, kpk, vpk, kc, vc, w["codec"], 1, 8, 32768)
-    print("scores max row rel err", check_rows(to_np(sc), ref_sc),
+    print("scores (max row rel err, max elem err)", check_scores(to_np(sc), ref_sc),
           "| out max row rel err", check_rows(to_np(out), ref_out))
 
 
@@ -133,4 +133,4 @@ def test_attend_llama_decode_slice():
     out, sc = tq.attend_decode(kc, vc, q, kpk, vpk, 131072, 2, want_scores=True)
     torch.cuda.synchronize()
     ref_out, ref_sc = _oracle_attention(to_np(q), kpk, vpk, kc, vc, p["codec"], 1, 2, 131072)
-    print("scores", check_rows(to_np(sc), ref_sc), "out", check_rows(to_np(out), ref_out))
+    print("scores", check_scores(to_np(sc), ref_sc), "out", check_rows(to_np(out), ref_out))

@@ -217,3 +217,60 @@ def test_encode_kv_one_launch_equals_two(d, kbits, vbits):
         assert torch.equal(x, y)
     check_prod(k.astype(np.float64), ka, kc, draws)
     check_mse(v.astype(np.float64), va, vc, vdraws)
+
+
+@pytest.mark.parametrize("d", [64, 128, 1536])
+@pytest.mark.parametrize("dtype", [np.float16, np.float32])
+def test_encode_non_finite_rows(d, dtype):
+    """Rows holding inf or NaN (keys and values, one call with both codecs)
+    get the zero vector's codes, sign bits and gamma, exactly as the oracle
+    encodes them, and store a non-finite norm of the oracle's kind (inf, or
+    NaN when a NaN is present); the finite rows around them follow the
+    ordinary parity rules."""
+    say("encode non-finite rows d=%d %s" % (d, np.dtype(dtype).name))
+    rng = np.random.default_rng(31 + d + (dtype == np.float32))
+    n = 37 if d == 1536 else 101
+    kb, vb = (2, 2) if d == 1536 else (4, 4)
+    x = rng.standard_normal((n, d)).astype(dtype)
+    y = rng.standard_normal((n, d)).astype(dtype)
+    for a in (x, y):
+        a[6] = 0.0
+    x[1, 3], x[2, 0], x[4, d - 1] = np.inf, -np.inf, np.nan
+    x[5, 1], x[5, 2] = np.inf, np.nan
+    y[3, 9], y[8, 0], y[n - 1, 5] = np.nan, np.inf, -np.inf
+    draws = synth.codec_draws(rng, d, m=d)
+    kc = make_codec(d, tq.TQ_PROD, kb, draws)
+    vc = make_codec(d, tq.TQ_MSE, vb, draws)
+    kout, vout = tq.encode_kv(kc, vc, torch.from_numpy(x).cuda(), torch.from_numpy(y).cuda())
+    torch.cuda.synchronize()
+    S = draws.S.astype(np.float64)
+    for a, out, codec in ((x, kout, kc), (y, vout, vc)):
+        a64 = a.astype(np.float64)
+        bad = ~np.all(np.isfinite(a64), axis=1)
+        cb = codec.code_bits
+        c, t = oracle.codebook(d, cb)
+        if codec.mode == tq.TQ_PROD:
+            enc = oracle.encode_prod(a64, draws.flip, c, t, S)
+            g = gpu_codes(out, d, cb, codec.m)
+            check_qjl({k: v[bad] for k, v in g.items()}, enc.z[bad], c, S)
+            check_prod(a64[~bad], _rows(out, ~bad), codec, draws)
+        else:
+            enc = oracle.encode_mse(a64, draws.flip, t)
+            g = gpu_codes(out, d, cb)
+            check_mse(a64[~bad], _rows(out, ~bad), codec, draws)
+        assert np.array_equal(g["idx"][bad], enc.idx[bad])
+        assert np.all(g["idx"][bad] == g["idx"][6])
+        assert np.array_equal(np.isnan(g["norm"][bad]), np.isnan(enc.norm[bad]))
+        assert np.all(np.isposinf(g["norm"][bad]) == np.isposinf(enc.norm[bad]))
+        assert g["norm"][6] == 0.0
+
+
+class _rows:
+    """The rows `keep` of a Packed, as host-side views for the checkers."""
+
+    def __init__(self, pk, keep):
+        sel = torch.from_numpy(np.flatnonzero(keep)).cuda()
+        self.idx = pk.idx[sel]
+        self.norm = pk.norm[sel]
+        self.qjl = pk.qjl[sel] if pk.qjl is not None else None
+        self.rnorm = pk.rnorm[sel] if pk.rnorm is not None else None

@@ -15,7 +15,7 @@ import torch
 import oracle
 import synth
 from oracle import split as SP
-from parity import (check_codes, check_norm, check_qjl, check_rows, gpu_codes, row_rel_err,
+from parity import (check_codes, check_norm, check_qjl, check_rows, check_scores, gpu_codes, row_rel_err,
                     to_np)
 
 pytestmark = pytest.mark.gpu
@@ -192,7 +192,7 @@ def test_split_attention_from_codes(b_hi, b_lo, G, n_q):
             got = out[b, g * G:(g + 1) * G].reshape(G * n_q, 128)
             check_rows(got, want, tol=1e-3)
             s_want = SP.estimate_split(qq, gk, 64, ko[0], ko[1]) / np.sqrt(128.0)
-            check_rows(scores[b, g * G:(g + 1) * G].reshape(G * n_q, ctx), s_want, tol=1e-3)
+            check_scores(scores[b, g * G:(g + 1) * G].reshape(G * n_q, ctx), s_want, tol=1e-3)
 
 
 @pytest.mark.parametrize("kr,vr", [((3, 2), (4, 3)), ((4, 3), (3, 2))])

@@ -7,7 +7,7 @@ import torch
 
 import oracle
 import synth
-from parity import check_codes, check_norm, check_qjl, check_rows, gpu_codes, to_np
+from parity import check_codes, check_norm, check_qjl, check_rows, check_scores, gpu_codes, to_np
 from test_gpu_scan import _check_topk
 
 pytestmark = pytest.mark.gpu
@@ -124,7 +124,7 @@ def test_wide_scan_and_top10(mode, bits):
     mat, ids, vals = tq.inner_product(codec, q, pk, n, top_k=10)
     torch.cuda.synchronize()
     ref = _oracle_scores(data["q"].numpy(), pk, codec, draws)
-    err = check_rows(to_np(mat).astype(np.float64), ref)
+    err = check_scores(to_np(mat).astype(np.float64), ref)
     _check_topk(to_np(ids), to_np(vals), ref, 10)
     print("max row rel err", err)
 

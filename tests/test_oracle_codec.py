@@ -216,3 +216,66 @@ def test_zero_vector():
     q = np.ones((1, d))
     assert estimate_ip(q, enc.idx, enc.norm, np.ones(d), c, sign=enc.sign,
                        rnorm=enc.rnorm, S=S)[0, 0] == 0.0
+
+
+def test_residual_from_codes_brute_force_and_cell_bounds():
+    """The conditional QJL check re-derives r = z - c[idx] from given codes.
+    Pinned three ways: element by element in plain Python on hand-edited
+    codes; each residual of the oracle's own codes lies inside its cell
+    (t_{k-1} - c_k <= r <= t_k - c_k, outer cells to -1 and +1); and, on the
+    oracle's own codes, |r| equals the stored gamma and the sign bits of
+    S r equal the stored ones.  A flipped sign, a shifted table index or a
+    transposed operand fails one of these."""
+    from oracle.codec import residual_from_codes
+    d = 16
+    c, t = codebook(d, 2)
+    rng = np.random.default_rng(21)
+    signs = np.where(rng.random(d) < 0.5, -1, 1)
+    S = rng.standard_normal((d, d))
+    x = rng.standard_normal((5, d))
+    enc = encode_prod(x, signs, c, t, S)
+    edited = enc.idx.copy()
+    edited[0, 3] = (edited[0, 3] + 1) % 4
+    edited[2, :] = 3 - edited[2, :]
+    edited[4, 7] = 0
+    r = residual_from_codes(enc.z, edited, c)
+    for n in range(5):
+        for k in range(d):
+            assert r[n, k] == enc.z[n, k] - c[edited[n, k]]
+    lo = np.concatenate([[-1.0], t])
+    hi = np.concatenate([t, [1.0]])
+    r0 = residual_from_codes(enc.z, enc.idx, c)
+    assert np.all(r0 >= lo[enc.idx] - c[enc.idx] - 1e-15)
+    assert np.all(r0 <= hi[enc.idx] - c[enc.idx] + 1e-15)
+    assert np.allclose(np.sqrt(np.sum(r0 * r0, axis=1)), enc.rnorm, rtol=1e-14, atol=0)
+    p = np.array([[sum(S[i, k] * r0[n, k] for k in range(d)) for i in range(d)] for n in range(5)])
+    assert np.array_equal((p >= 0).astype(np.uint8), enc.sign)
+
+
+def test_non_finite_rows_take_the_zero_vector_codes():
+    """A row holding inf or NaN gets the zero vector's codes (idx, sign
+    bits, gamma) and keeps its non-finite norm: inf for an infinite element,
+    NaN when a NaN is present.  Other rows are unaffected."""
+    d = 32
+    c, t = codebook(d, 3)
+    rng = np.random.default_rng(5)
+    signs = np.where(rng.random(d) < 0.5, -1, 1)
+    S = rng.standard_normal((d, d))
+    x = rng.standard_normal((6, d))
+    x[1, 4] = np.inf
+    x[2, 0] = -np.inf
+    x[3, 9] = np.nan
+    x[4, 1], x[4, 2] = np.inf, np.nan
+    x[5] = 0.0
+    enc = encode_prod(x, signs, c, t, S)
+    mse = encode_mse(x, signs, t)
+    zero = encode_prod(np.zeros((1, d)), signs, c, t, S)
+    for n in (1, 2, 3, 4, 5):
+        assert np.array_equal(enc.idx[n], zero.idx[0]) and np.array_equal(mse.idx[n], zero.idx[0])
+        assert np.array_equal(enc.sign[n], zero.sign[0])
+        assert enc.rnorm[n] == zero.rnorm[0]
+    assert np.isposinf(enc.norm[1]) and np.isposinf(enc.norm[2])
+    assert np.isnan(enc.norm[3]) and np.isnan(enc.norm[4]) and enc.norm[5] == 0.0
+    assert np.array_equal(mse.norm[1:3], enc.norm[1:3])
+    alone = encode_prod(x[:1], signs, c, t, S)
+    assert np.array_equal(alone.idx, enc.idx[:1]) and alone.norm[0] == enc.norm[0]

@@ -274,3 +274,21 @@ def test_restart_keeps_the_first_on_rounding_ties():
     pts = F.quadrature(d)
     a = F.lloyd(F.spiral_init(d, 2, 0.0), pts)
     assert np.allclose(book(d, 2), a, atol=0)
+
+
+def test_non_finite_row_codes_like_the_zero_row():
+    """A row holding inf or NaN takes z = 0 (the zero row's codes) and
+    keeps its non-finite norm."""
+    d = 64
+    code = F.fibquant_codebook(d, 16)
+    rng = np.random.default_rng(6)
+    signs = np.where(rng.random(d) < 0.5, -1, 1)
+    x = rng.standard_normal((4, d))
+    x[1, 5] = np.inf
+    x[2, 0] = np.nan
+    x[3] = 0.0
+    idx, nu, z = F.encode_vq(x, signs, code)
+    assert np.all(z[1:] == 0.0)
+    assert np.array_equal(idx[1], idx[3]) and np.array_equal(idx[2], idx[3])
+    assert np.isposinf(nu[1]) and np.isnan(nu[2]) and nu[3] == 0.0
+    assert np.all(np.isfinite(z[0])) and nu[0] > 0
