@@ -247,7 +247,11 @@ def test_split_attention_validation():
     with pytest.raises(tq.TQError):         # 32 query rows per KV head
         tq.attend_split(ks, vs, q, kp, vp, 64, 1)
     odd = tq.SplitCodec(*half_codec(rng, 4, True)[:1], *half_codec(rng, 2, True)[:1])
+    kodd, _ = tq.encode_split(odd, None, torch.zeros((64, 128), dtype=torch.float16, device="cuda"),
+                              None)
     with pytest.raises(tq.TQError):         # table widths (3, 1): no kernel
+        tq.attend_split(odd, vs, q[:, :4], kodd, vp, 64, 1)
+    with pytest.raises(ValueError):         # codes packed for another codec: caught in the binding
         tq.attend_split(odd, vs, q[:, :4], kp, vp, 64, 1)
 
 
