@@ -60,7 +60,9 @@ enum {
   TQ_ERR_UNSUPPORTED = -2,   /* valid request this build has no kernel for */
   TQ_ERR_NOT_CONVERGED = -3, /* codebook iteration hit its limit */
   TQ_ERR_HIP = -4,           /* the HIP runtime reported a launch error */
-  TQ_ERR_WORKSPACE = -5      /* workspace null or smaller than required */
+  TQ_ERR_WORKSPACE = -5,     /* workspace null or smaller than required */
+  TQ_ERR_TOO_LARGE = -6      /* request needs more than the fixed scratch of
+                                tq_attend_decode_noalloc */
 };
 
 enum { TQ_MSE = 0, TQ_PROD = 1 };   /* codec mode */
@@ -327,6 +329,27 @@ int tq_attend_decode(const tq_codec* kc, const tq_codec* vc, const void* q,
                      const tq_packed* v, int64_t ctx, float scale, float* out,
                      float* scores_out, void* workspace,
                      size_t workspace_bytes, tq_stream_t stream);
+
+/* The same attention for callers that cannot allocate device memory (code
+ * under HIP graph capture, serving loops or harnesses that forbid
+ * allocation): arguments and results as tq_attend_decode, without the
+ * workspace.  The kernels' scratch is a fixed device array inside the
+ * library, TQ_NOALLOC_SCRATCH_BYTES per GPU, which each GPU the library runs
+ * on holds until the process ends; its address is looked up the first time a
+ * device calls in.  The call itself allocates nothing.
+ * A request whose tq_attend_decode_workspace(...) exceeds
+ * TQ_NOALLOC_SCRATCH_BYTES returns TQ_ERR_TOO_LARGE before anything is
+ * enqueued.  All calls on one GPU share the array: calls that overlap in
+ * time on one GPU (other streams, other host threads) race and must be
+ * serialized by the caller.  Returns the statuses of tq_attend_decode, or
+ * TQ_ERR_TOO_LARGE, or TQ_ERR_HIP when the scratch address cannot be
+ * obtained. */
+#define TQ_NOALLOC_SCRATCH_BYTES (16u << 20)
+int tq_attend_decode_noalloc(const tq_codec* kc, const tq_codec* vc, const void* q,
+                             int q_dtype, int batch, int n_q, int hq, int hkv,
+                             const tq_rope* q_rope, const tq_packed* k,
+                             const tq_packed* v, int64_t ctx, float scale, float* out,
+                             float* scores_out, tq_stream_t stream);
 
 /* Attention from outlier-split codes: the keys and values of each token are
  * two d = 64 codecs over channels [0, 64) and [64, 128) (tq_encode_split), so

@@ -22,7 +22,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtq.so")
 
 TQ_OK, TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED = 0, -1, -2
-TQ_ERR_NOT_CONVERGED, TQ_ERR_HIP, TQ_ERR_WORKSPACE = -3, -4, -5
+TQ_ERR_NOT_CONVERGED, TQ_ERR_HIP, TQ_ERR_WORKSPACE, TQ_ERR_TOO_LARGE = -3, -4, -5, -6
+NOALLOC_SCRATCH_BYTES = 16 << 20
 TQ_MSE, TQ_PROD = 0, 1
 TQ_F16, TQ_F32 = 0, 1
 
@@ -31,7 +32,7 @@ EXPORTS = ("tq_status_string", "tq_build_codebook", "tq_codec_init", "tq_encode_
            "tq_outlier_order",
            "tq_build_vq_codebook", "tq_vq_codec_init", "tq_vq_search_build", "tq_encode_vq",
            "tq_decode_vq",
-           "tq_attend_decode_workspace", "tq_attend_decode",
+           "tq_attend_decode_workspace", "tq_attend_decode", "tq_attend_decode_noalloc",
            "tq_inner_product_workspace", "tq_inner_product")
 
 
@@ -121,6 +122,10 @@ def lib():
     L.tq_attend_decode.argtypes = [ctypes.POINTER(TQCodec), ctypes.POINTER(TQCodec), P, I, I, I, I, I,
                                    ctypes.POINTER(TQRope), ctypes.POINTER(TQPacked),
                                    ctypes.POINTER(TQPacked), I64, F, P, P, P, SZ, P]
+    L.tq_attend_decode_noalloc.restype = I
+    L.tq_attend_decode_noalloc.argtypes = [ctypes.POINTER(TQCodec), ctypes.POINTER(TQCodec), P, I, I, I,
+                                           I, I, ctypes.POINTER(TQRope), ctypes.POINTER(TQPacked),
+                                           ctypes.POINTER(TQPacked), I64, F, P, P, P]
     L.tq_inner_product_workspace.restype = SZ
     L.tq_inner_product_workspace.argtypes = [I64, I64, I, I]
     L.tq_inner_product.restype = I
@@ -624,6 +629,36 @@ def attend_decode(kcodec, vcodec, q, kpk, vpk, ctx, hkv, scale=0.0, rope=None, o
                                 workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "tq_attend_decode")
     return (out, scores) if want_scores else out
+
+
+@_on_stream
+def attend_decode_noalloc(kcodec, vcodec, q, kpk, vpk, ctx, hkv, out, scale=0.0, rope=None,
+                          scores_out=None, *, stream=None):
+    """attend_decode through the library's allocation-free entry point: no
+    workspace (the kernels use the library's fixed per-GPU scratch), and the
+    caller passes the output (and optional scores) buffers, so this call
+    allocates nothing either.  Calls that overlap in time on one GPU race."""
+    _device_tensor(q, "q")
+    if q.dim() != 4:
+        raise ValueError("q must be [batch, hq, n_q, d]")
+    batch, hq, n_q, d = q.shape
+    if d != kcodec.d or d != vcodec.d:
+        raise ValueError("q rows hold %d elements, the codecs d = %d / %d" % (d, kcodec.d, vcodec.d))
+    _check_heads(hq, hkv, ctx)
+    _check_packed(kpk, kcodec, batch * hkv * ctx, "kpk")
+    _check_packed(vpk, vcodec, batch * hkv * ctx, "vpk")
+    _out_tensor(out, "out", (batch, hq, n_q, d), torch.float32)
+    if scores_out is not None:
+        _out_tensor(scores_out, "scores_out", (batch, hq, n_q, ctx), torch.float32)
+    r = TQRope(float(rope[0]), int(rope[1]), 0) if rope is not None else None
+    st = lib().tq_attend_decode_noalloc(ctypes.byref(kcodec.struct), ctypes.byref(vcodec.struct),
+                                        _ptr(q), _dtype_code(q), batch, n_q, hq, hkv,
+                                        ctypes.byref(r) if r is not None else None,
+                                        ctypes.byref(kpk.struct), ctypes.byref(vpk.struct),
+                                        int(ctx), float(scale), _ptr(out), _ptr(scores_out),
+                                        _stream(stream))
+    _check(st, "tq_attend_decode_noalloc")
+    return out
 
 
 def inner_product_workspace_bytes(n_q, n, d, top_k):

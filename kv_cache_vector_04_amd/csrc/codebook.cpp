@@ -127,6 +127,7 @@ extern "C" const char* tq_status_string(int status) {
     case TQ_ERR_NOT_CONVERGED: return "codebook iteration did not converge";
     case TQ_ERR_HIP: return "HIP runtime error";
     case TQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case TQ_ERR_TOO_LARGE: return "request needs more than the library's fixed scratch";
     default: return "unknown status";
   }
 }

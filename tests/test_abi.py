@@ -380,7 +380,8 @@ def test_stream_is_keyword_only():
     import inspect
     kinds = {}
     for fn in (tq.encode_kv, tq.encode_vq, tq.decode_vq, tq.decode_kv, tq.encode_split,
-               tq.decode_split, tq.attend_split, tq.attend_decode, tq.inner_product):
+               tq.decode_split, tq.attend_split, tq.attend_decode, tq.attend_decode_noalloc,
+               tq.inner_product):
         kinds[fn.__name__] = inspect.signature(fn.__wrapped__).parameters["stream"].kind
     assert set(kinds.values()) == {inspect.Parameter.KEYWORD_ONLY}, kinds
     with pytest.raises(TypeError):
