@@ -740,7 +740,10 @@ hipError_t launch_decode(const tq_codec& kc, const tq_codec& vc, const void* q, 
       p.theta[i] = std::pow((double)rope.base, -2.0 * i / (double)d);
   const dim3 grid((unsigned)groups, (unsigned)splits);
   hipError_t e;
-  if (d == 128) e = dec_pick_k<128>(kc.code_bits, vc.code_bits, p, grid, stream);
+  if (d == 128 && decode_mfma_supported(kc, vc))
+    e = launch_decode_mfma(kc, vc, q, q_dtype, n_q, hq, hkv, rope, k, v, ctx, scale, scores_out,
+                           p.part, nchunks, splits, split_len, grid, stream);
+  else if (d == 128) e = dec_pick_k<128>(kc.code_bits, vc.code_bits, p, grid, stream);
   else if (d == 64) e = dec_pick_k<64>(kc.code_bits, vc.code_bits, p, grid, stream);
   else return hipErrorInvalidValue;
   if (e != hipSuccess) return e;

@@ -80,6 +80,14 @@ hipError_t launch_attend_mq(const tq_codec& kc, const tq_codec& vc, const void* 
                             const tq_packed& k, const tq_packed& v, int64_t ctx, float scale,
                             float* out, float* scores_out, void* workspace, hipStream_t stream);
 size_t decode_workspace_bytes(int batch, int n_q, int hq, int hkv, int64_t ctx, int d);
+// few-row decode at d = 128 on the matrix cores (decode_mfma.hip): writes the
+// same per-range records as the decode kernel, for the same merge
+bool decode_mfma_supported(const tq_codec& kc, const tq_codec& vc);
+hipError_t launch_decode_mfma(const tq_codec& kc, const tq_codec& vc, const void* q, int q_dtype,
+                              int n_q, int hq, int hkv, const RopeHost& rope, const tq_packed& k,
+                              const tq_packed& v, int64_t ctx, float scale, float* scores_out,
+                              float* part, int nchunks, int splits, int64_t split_len, dim3 grid,
+                              hipStream_t stream);
 hipError_t launch_decode(const tq_codec& kc, const tq_codec& vc, const void* q, int q_dtype,
                          int batch, int n_q, int hq, int hkv, const RopeHost& rope,
                          const tq_packed& k, const tq_packed& v, int64_t ctx, float scale,
