@@ -289,7 +289,7 @@ def main():
     dom = max(parts, key=lambda p: parts[p][0])
     t_dom, b_dom = parts[dom]
     roof = {"kernel": {"encode": "encode_kv_half_kernel<128,3,4> (keys prod + values mse, fp16)",
-                       "attend": "decode_kernel<128,3,4> + merge_kernel<128>"}[dom],
+                       "attend": "decode_mfma_kernel<3,4,8> + merge_kernel<128>"}[dom],
             "bound": "hbm", "achieved": b_dom / t_dom / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": b_dom / t_dom / 1e9 / HBM_PEAK_GBS, "traffic": counter_traffic(dom)}
 
@@ -394,7 +394,7 @@ def bench_layers(a, torch, synth, tq, dev):
     kname = {"encode": "encode_kv_half_kernel<128,2,3> (keys prod + values mse, one launch)"
                        if a.workload == "llama_prefill" else
                        "encode_kernel<64,2,prod,RoPE> + encode_half_kernel<64,3,mse>",
-             "attend": "decode_kernel<128,2,3> + merge_kernel<128>"
+             "attend": "decode_mfma_kernel<2,3,8> + merge_kernel<128>"
                        if a.workload == "llama_prefill" else "attend_mq_kernel<2,3>"}[dom]
     roof = {"kernel": kname, "bound": "hbm", "achieved": parts[dom][1] / parts[dom][0] / 1e9,
             "peak": HBM_PEAK_GBS, "unit": "GB/s",
