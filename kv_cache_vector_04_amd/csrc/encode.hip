@@ -1,4 +1,6 @@
-// TurboQuant encode for gfx950, d = 64 or 128: one vector per lane.
+// TurboQuant encode for gfx950, d = 64 or 128: one vector per lane (fp32
+// input at d = 64, RoPE keys) or two lanes per vector (fp16 input, and fp32
+// input at d = 128; see the layout notes further down).
 //
 // Per vector ("FibQuant", "1. Enunciato del Problema" and "2.3 Codifica e
 // Decodifica"; "Google presenta TurboQuant", "La mecánica geométrica de
@@ -393,7 +395,9 @@ __global__ __launch_bounds__(kEncWaves * kWave) void encode_kernel(EncodeParams 
 }
 
 // ---------------------------------------------------------------------------
-// fp16 input without RoPE: two lanes per vector.  Lane l of a wave owns
+// fp16 input without RoPE, and fp32 input at d = 128: two lanes per vector
+// (fp32 rows take the path of f32_rotate_half below up to the rotated
+// coordinates, then the same quantizer and projection).  Lane l of a wave owns
 // token 32 tile + l%32 and the coordinate half h = l/32 (coordinates
 // h d/2 .. h d/2 + d/2 - 1), which halves the registers a vector needs and
 // lets more waves hide the HBM latency.  The butterfly stages commute; the
@@ -411,11 +415,13 @@ __global__ __launch_bounds__(kEncWaves * kWave) void encode_kernel(EncodeParams 
 // per CU; eight waves each at two waves per SIMD leave the registers for
 // loading the next tile's input while the current one is processed.  mse:
 // small workgroups at four waves per SIMD (a prefetch measured no faster).
-template <bool PROD>
+template <bool PROD, bool F32IN = false>
 struct HalfLaunch {
-  static constexpr bool kPrefetch = PROD;
+  static constexpr bool kPrefetch = PROD && !F32IN;
   static constexpr int kWaves = PROD ? 8 : 4;
-  static constexpr int kMinWavesPerEU = PROD ? 2 : 4;
+  // (fp32 mse rows hold 64 loaded floats per lane: more than four waves'
+  // share of the registers)
+  static constexpr int kMinWavesPerEU = PROD || F32IN ? 2 : 4;
 };
 
 // v from the low half plus v from the high half, in every lane
@@ -426,12 +432,13 @@ __device__ __forceinline__ float cross_sum(float v) {
 }
 
 // LDS tables of one codec for the two-lanes-per-vector encoder
-template <int D, int CB, bool PROD, bool MROT = false>
+template <int D, int CB, bool PROD, bool MROT = false, bool F32IN = false>
 struct HalfTables {
   static constexpr int FRAGS = (D / 32) * (D / 16);
   float cent[16];
   float2 lut[CB >= 3 ? kLutMax : 1];
   uint4 hmask[MROT ? 1 : D / 8];
+  uint4 fmask[F32IN ? D / 4 : 1];       // fp32 input: bit 31 of coordinate i's word set when D_ii = -1
   uint4 hd[MROT ? FRAGS * kWave : 1];   // H D as A fragments (rotation on the matrix cores)
   uint4 frag[PROD ? FRAGS * 2 * kWave : 1];
 };
@@ -439,9 +446,9 @@ struct HalfTables {
 // The tables from the codec (all nthr threads of the workgroup take part;
 // the caller synchronizes afterwards).  kp: p in the kernel argument
 // segment, for indexing its arrays with run-time indices.
-template <int D, int CB, bool PROD, bool MROT = false>
+template <int D, int CB, bool PROD, bool MROT = false, bool F32IN = false>
 __device__ __forceinline__ void half_setup(const EncodeParams& p, const EncodeParams* kp,
-                                           HalfTables<D, CB, PROD, MROT>& T, int tid, int nthr) {
+                                           HalfTables<D, CB, PROD, MROT, F32IN>& T, int tid, int nthr) {
   constexpr int NLEV = 1 << CB;
   constexpr int NTH = NLEV - 1;
   constexpr int HALF = D / 2;
@@ -454,6 +461,13 @@ __device__ __forceinline__ void half_setup(const EncodeParams& p, const EncodePa
   if (!MROT && tid >= 64 && tid < 64 + NP / 2)
     T.hmask[tid - 64] = make_uint4(kp->hflip[4 * (tid - 64)], kp->hflip[4 * (tid - 64) + 1],
                                    kp->hflip[4 * (tid - 64) + 2], kp->hflip[4 * (tid - 64) + 3]);
+  if (F32IN && tid >= 128 && tid < 128 + D / 4) {
+    const int i = 4 * (tid - 128);
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = ((kp->codec.flip[(i + e) >> 5] >> ((i + e) & 31)) & 1u) << 31;
+    T.fmask[tid - 128] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
   if constexpr (USE_LUT) {
     const float a = p.lut_a, b = p.lut_b;
     for (int g = tid; g < p.lut_g; g += nthr) {
@@ -521,6 +535,89 @@ __device__ __forceinline__ void half_setup(const EncodeParams& p, const EncodePa
   }
 }
 
+// largest of v in the low and the high half, in every lane
+__device__ __forceinline__ float cross_max(float v) {
+  uint32_t a = __float_as_uint(v), b = a;
+  swap_halves(a, b);
+  return fmaxf(__uint_as_float(a), __uint_as_float(b));
+}
+
+// fp32 input, two lanes per vector: lane half h loads coordinates
+// h d/2 .. h d/2 + d/2 - 1 of its row; the pair forms nu, flips the signs
+// and runs every butterfly stage, the one across the halves through
+// v_permlane32_swap and the others in registers.  When the squares leave
+// the normal fp32 range the row is first scaled exactly by the power of two
+// that brings its largest entry into [0.5, 1): the return value is the norm
+// of the scaled row and pre_inv the power of two that undoes the scaling.
+// A row with an inf or NaN element comes back as the zero vector with a
+// non-finite norm (inf, or NaN when an element is NaN).  Both lanes of a
+// pair see the same sums and take the same branches.
+template <int D>
+__device__ __forceinline__ float f32_rotate_half(const EncodeParams& p, const uint4* fmask, int64_t row,
+                                                 bool valid, float sgn, float (&x)[D / 2], float& pre_inv) {
+  constexpr int HALF = D / 2;
+  const int h = (threadIdx.x & 63) >> 5;
+  if (valid) {
+    const float4* src = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p.x) + row * p.x_stride + h * HALF);
+#pragma unroll
+    for (int j = 0; j < HALF / 4; ++j) {
+      const float4 v = src[j];
+      x[4 * j] = v.x; x[4 * j + 1] = v.y; x[4 * j + 2] = v.z; x[4 * j + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < HALF; ++i) x[i] = 0.f;
+  }
+  float nu2 = cross_sum(sum_squares<HALF>(x));
+  pre_inv = 1.f;
+  if (!(nu2 >= 0x1p-100f && nu2 <= 0x1p100f)) {
+    // a NaN element makes the sum NaN (fmaxf below would skip it)
+    const bool has_nan = !(nu2 == nu2);
+    float mx = 0.f;
+#pragma unroll
+    for (int i = 0; i < HALF; ++i) mx = fmaxf(mx, fabsf(x[i]));
+    mx = cross_max(mx);
+    if (has_nan || !(mx <= 3.4e38f)) {
+#pragma unroll
+      for (int i = 0; i < HALF; ++i) x[i] = 0.f;
+    } else if (mx > 0.f) {
+      int e;
+      frexpf(mx, &e);
+      const float sc = ldexpf(1.f, -e);
+      pre_inv = ldexpf(1.f, e);
+#pragma unroll
+      for (int i = 0; i < HALF; ++i) x[i] *= sc;
+      nu2 = cross_sum(sum_squares<HALF>(x));
+    }
+  }
+  // sign flip, then the stage across the halves: the low lane keeps
+  // x_i + x_{i + d/2}, the high lane x_i - x_{i + d/2}
+#pragma unroll
+  for (int j4 = 0; j4 < HALF / 4; ++j4) {
+    const uint4 m4 = fmask[h * (HALF / 4) + j4];
+    const uint32_t ms[4] = {m4.x, m4.y, m4.z, m4.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j = 4 * j4 + e;
+      uint32_t a = __float_as_uint(x[j]) ^ ms[e], b = a;
+      swap_halves(a, b);   // a: the low lane's value, b: the high lane's value
+      x[j] = fmaf(__uint_as_float(b), sgn, __uint_as_float(a));
+    }
+  }
+#pragma unroll
+  for (int hh = 1; hh < HALF; hh <<= 1) {
+#pragma unroll
+    for (int i = 0; i < HALF; ++i) {
+      if ((i & hh) == 0) {
+        const float a = x[i], b = x[i + hh];
+        x[i] = a + b;
+        x[i + hh] = a - b;
+      }
+    }
+  }
+  return sqrtf(nu2);
+}
+
 // Loads the input of tile t for this lane (rows past the end read as zeros).
 template <int D>
 __device__ __forceinline__ void half_load(const EncodeParams& p, int64_t t, uint32_t (&dst)[D / 4]) {
@@ -543,9 +640,10 @@ __device__ __forceinline__ void half_load(const EncodeParams& p, int64_t t, uint
 // One wave's tiles: tile, tile + tstride, ...  With PF the input of the
 // next tile is loaded while the current one is processed, and nxt holds
 // the first tile's input on entry.
-template <int D, int CB, bool PROD, bool PF, bool MROT = false>
-__device__ __forceinline__ void half_tiles(const EncodeParams& p, const HalfTables<D, CB, PROD, MROT>& T,
+template <int D, int CB, bool PROD, bool PF, bool MROT = false, bool F32IN = false>
+__device__ __forceinline__ void half_tiles(const EncodeParams& p, const HalfTables<D, CB, PROD, MROT, F32IN>& T,
                                            int64_t tile, int64_t tstride, uint32_t (&nxt)[D / 4]) {
+  static_assert(!F32IN || (!PF && !MROT), "fp32 input: no prefetch, butterflies in registers");
   constexpr int NLEV = 1 << CB;
   constexpr int NTH = NLEV - 1;
   constexpr int HALF = D / 2;              // coordinates per lane
@@ -568,6 +666,14 @@ __device__ __forceinline__ void half_tiles(const EncodeParams& p, const HalfTabl
   for (; tile < ntiles; tile += tstride) {
     const int64_t row = tile * 32 + (lane & 31);
     const bool valid = row < p.n_rows;
+    float x[HALF];
+    float nu_s, nu_out;
+    if constexpr (F32IN) {
+      // x may come back scaled by a power of two (nu_s is its norm)
+      float pre_inv;
+      nu_s = f32_rotate_half<D>(p, T.fmask, row, valid, sgn, x, pre_inv);
+      nu_out = nu_s * pre_inv;
+    } else {
     uint32_t u[NP];
     if (PF) {
 #pragma unroll
@@ -602,9 +708,9 @@ __device__ __forceinline__ void half_tiles(const EncodeParams& p, const HalfTabl
 #pragma unroll
       for (int j = 0; j < NP; ++j) u[j] = 0u;
     }
-    const float nu_s = sqrtf(nu2);
+    nu_s = sqrtf(nu2);
+    nu_out = nu_s;
 
-    float x[HALF];
     if constexpr (MROT) {
       // y = H D x on the matrix cores: B = the lane's own input (k slot j of
       // lane half h at step ks is coordinate (d/2) h + 8 ks + j), A = the
@@ -659,6 +765,7 @@ __device__ __forceinline__ void half_tiles(const EncodeParams& p, const HalfTabl
         }
       }
     }
+    }
     __builtin_amdgcn_sched_barrier(0);
 
     const bool live = nu_s > 0.f && nu_s <= 3.0e38f;
@@ -695,7 +802,7 @@ __device__ __forceinline__ void half_tiles(const EncodeParams& p, const HalfTabl
       for (int i = 0; i < HALF; ++i) quantize(i);
       if (valid) {
         store_words<HW, HALIGN>(idx_dst, words);
-        if (h == 0) p.norm[row] = nu_s;
+        if (h == 0) p.norm[row] = nu_out;
       }
     } else {
       uint32_t bh[KS][4], bl[KS][4];
@@ -721,7 +828,7 @@ __device__ __forceinline__ void half_tiles(const EncodeParams& p, const HalfTabl
       }
       if (valid) {
         store_words<HW, HALIGN>(idx_dst, words);
-        if (h == 0) p.norm[row] = nu_s;
+        if (h == 0) p.norm[row] = nu_out;
       }
       const float gamma2 = cross_sum(g2[0] + g2[1]);
       if (valid && h == 0) p.rnorm[row] = sqrtf(gamma2) * (1.f / 256.f);
@@ -782,11 +889,11 @@ __device__ __forceinline__ void half_tiles(const EncodeParams& p, const HalfTabl
   }
 }
 
-template <int D, int CB, bool PROD>
-__global__ __launch_bounds__(HalfLaunch<PROD>::kWaves * kWave, HalfLaunch<PROD>::kMinWavesPerEU) void encode_half_kernel(EncodeParams p) {
-  constexpr int kHalfWaves = HalfLaunch<PROD>::kWaves;
-  constexpr bool PF = HalfLaunch<PROD>::kPrefetch;
-  __shared__ HalfTables<D, CB, PROD> T;
+template <int D, int CB, bool PROD, bool F32IN>
+__global__ __launch_bounds__((HalfLaunch<PROD, F32IN>::kWaves * kWave), (HalfLaunch<PROD, F32IN>::kMinWavesPerEU)) void encode_half_kernel(EncodeParams p) {
+  constexpr int kHalfWaves = HalfLaunch<PROD, F32IN>::kWaves;
+  constexpr bool PF = HalfLaunch<PROD, F32IN>::kPrefetch;
+  __shared__ HalfTables<D, CB, PROD, false, F32IN> T;
   const int tid = threadIdx.x;
   const EncodeParams* kp = (const EncodeParams*)__builtin_amdgcn_kernarg_segment_ptr();
   const int64_t tstride = (int64_t)gridDim.x * kHalfWaves;
@@ -794,9 +901,9 @@ __global__ __launch_bounds__(HalfLaunch<PROD>::kWaves * kWave, HalfLaunch<PROD>:
   uint32_t nxt[D / 4];
   // the first tile's input is in flight during the set-up
   if (PF) half_load<D>(p, tile, nxt);
-  half_setup<D, CB, PROD>(p, kp, T, tid, blockDim.x);
+  half_setup<D, CB, PROD, false, F32IN>(p, kp, T, tid, blockDim.x);
   __syncthreads();
-  half_tiles<D, CB, PROD, PF>(p, T, tile, tstride, nxt);
+  half_tiles<D, CB, PROD, PF, false, F32IN>(p, T, tile, tstride, nxt);
 }
 
 // Keys (prod) and values (mse) of one call in one launch.  Each SIMD runs
@@ -838,15 +945,15 @@ __global__ __launch_bounds__((kKVKeyWaves + kKVValWaves) * kWave, 3) void encode
     half_tiles<D, CBV, false, true, kKVRotV>(pp.v, TV, vtile, (int64_t)gridDim.x * kKVValWaves, nxt);
 }
 
-template <int D, int CB, bool PROD>
+template <int D, int CB, bool PROD, bool F32IN>
 static hipError_t run_half(const EncodeParams& p, hipStream_t stream) {
-  constexpr int kHalfWaves = HalfLaunch<PROD>::kWaves;
+  constexpr int kHalfWaves = HalfLaunch<PROD, F32IN>::kWaves;
   // occupancy depends only on the kernel's resources (one code object for
   // every device): computed once, read by any host thread
   static std::atomic<int> per_cu{0};
   if (per_cu.load(std::memory_order_relaxed) == 0) {
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, encode_half_kernel<D, CB, PROD>,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, encode_half_kernel<D, CB, PROD, F32IN>,
                                                      kHalfWaves * kWave, 0) != hipSuccess || nb < 1)
       nb = 1;
     per_cu.store(nb, std::memory_order_relaxed);
@@ -856,18 +963,18 @@ static hipError_t run_half(const EncodeParams& p, hipStream_t stream) {
   const int64_t cap = (int64_t)device_cu_count() * per_cu.load(std::memory_order_relaxed);
   if (blocks > cap) blocks = cap;
   if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL((encode_half_kernel<D, CB, PROD>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((encode_half_kernel<D, CB, PROD, F32IN>), dim3((unsigned)blocks),
                      dim3(kHalfWaves * kWave), 0, stream, p);
   return hipGetLastError();
 }
 
-template <int D, bool PROD>
+template <int D, bool PROD, bool F32IN = false>
 static hipError_t pick_half(int cb, const EncodeParams& p, hipStream_t s) {
   switch (cb) {
-    case 1: return run_half<D, 1, PROD>(p, s);
-    case 2: return run_half<D, 2, PROD>(p, s);
-    case 3: return run_half<D, 3, PROD>(p, s);
-    case 4: return run_half<D, 4, PROD>(p, s);
+    case 1: return run_half<D, 1, PROD, F32IN>(p, s);
+    case 2: return run_half<D, 2, PROD, F32IN>(p, s);
+    case 3: return run_half<D, 3, PROD, F32IN>(p, s);
+    case 4: return run_half<D, 4, PROD, F32IN>(p, s);
   }
   return hipErrorInvalidValue;
 }
@@ -900,8 +1007,13 @@ static hipError_t pick_rest(const tq_codec& c, int dtype, bool rope, const Encod
   const bool prod = c.mode == TQ_PROD;
   if (dtype == TQ_F32) {
     if (rope) return hipErrorInvalidValue;  // RoPE inputs are fp16 in this build
-    return prod ? pick_cb<D, true, float, false>(c.code_bits, p, s)
-                : pick_cb<D, false, float, false>(c.code_bits, p, s);
+    // d = 128: two lanes per vector (one lane would need more than 256
+    // registers for the row, its codes and the projection's operands)
+    if constexpr (D == 128)
+      return prod ? pick_half<D, true, true>(c.code_bits, p, s) : pick_half<D, false, true>(c.code_bits, p, s);
+    else
+      return prod ? pick_cb<D, true, float, false>(c.code_bits, p, s)
+                  : pick_cb<D, false, float, false>(c.code_bits, p, s);
   }
   if (rope) {
     if constexpr (D == 64)

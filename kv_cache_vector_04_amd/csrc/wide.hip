@@ -65,6 +65,8 @@ constexpr H12Signs make_h12() {
 __device__ constexpr H12Signs kH12 = make_h12();
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 #define TQ_KARG(P, FIELD) \
   ((const char*)__builtin_amdgcn_kernarg_segment_ptr() + offsetof(P, FIELD))
@@ -520,7 +522,10 @@ __global__ __launch_bounds__(64 * kSWaves, 2) void wide_scan_kernel(WScanParams 
   __shared__ uint32_t s_ph[NP];
   __shared__ uint32_t s_pl[NP];
   __shared__ u32x4 s_pm[256];       // eight bits -> eight fp16 +-1
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
+  // (the wave index through readfirstlane: a scalar, so that the row bases
+  // derived from it stay in scalar registers)
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   if constexpr (CB > 1) {
     const uint32_t* chl = reinterpret_cast<const uint32_t*>(TQ_KARG(WScanParams, chl));
     for (int e = tid; e < NP; e += 64 * kSWaves) {
@@ -531,28 +536,42 @@ __global__ __launch_bounds__(64 * kSWaves, 2) void wide_scan_kernel(WScanParams 
   }
   for (int e = tid; e < 256; e += 64 * kSWaves) s_pm[e] = __builtin_bit_cast(u32x4, pm1_frag((uint32_t)e));
   __syncthreads();
-  const int64_t QB = (p.n_q + 31) / 32;
-  const int64_t b = blockIdx.x;
-  int64_t qb, rt;
+  // (32-bit index math, then readfirstlane: the divisions run on the vector
+  // unit, and their uniform results go back to scalar registers)
+  const uint32_t QB = (uint32_t)((p.n_q + 31) / 32);
+  const uint32_t b = blockIdx.x;
+  uint32_t qb32, rt32;
   if (QB % 8 == 0) {
     // each XCD keeps one eighth of the query planes in its L2
-    const int64_t per = QB / 8, k = b / 8;
-    qb = (b % 8) * per + k % per;
-    rt = k / per;
+    const uint32_t per = QB / 8, k = b / 8;
+    qb32 = (b % 8) * per + k % per;
+    rt32 = k / per;
   } else {
-    qb = b % QB;
-    rt = b / QB;
+    qb32 = b % QB;
+    rt32 = b / QB;
   }
+  const int64_t qb = (uint32_t)__builtin_amdgcn_readfirstlane((int)qb32);
+  const int64_t rt = (uint32_t)__builtin_amdgcn_readfirstlane((int)rt32);
   const int64_t r0 = rt * kSRows + wave * 32 * kSRB;
   constexpr int RB = kWD * CB / 8;
-  const uint8_t* crow[kSRB];
-  const uint8_t* srow[kSRB];
+  // Buffer descriptors over the workgroup's rows of the code and sign
+  // planes: 32-bit offsets (a lane's row and lane half in the vector
+  // offset, which the range check covers), and rows past n read as zero.
+  constexpr int kRsrcWord3 = 0x00020000;
+  const int64_t wrow = rt * kSRows;
+  const uint32_t wrows = (uint32_t)(p.n - wrow < kSRows ? p.n - wrow : kSRows);
+  const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.idx + wrow * RB), (short)0, (int)(wrows * RB), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      PROD ? (void*)(p.qjl + wrow * (kWD / 8)) : (void*)p.idx, (short)0, PROD ? (int)(wrows * (kWD / 8)) : 0,
+      kRsrcWord3);
+  // sign-plane offset of a lane's row and half; the code-plane offset is
+  // CB times it
+  uint32_t soff[kSRB];
 #pragma unroll
   for (int rb = 0; rb < kSRB; ++rb) {
-    const int64_t j = r0 + 32 * rb + (lane & 31);
-    const int64_t jr = j < p.n ? j : 0;
-    crow[rb] = p.idx + jr * RB;
-    srow[rb] = PROD ? p.qjl + jr * (kWD / 8) : nullptr;
+    const uint32_t jr = (uint32_t)(wave * 32 * kSRB + 32 * rb + (lane & 31));
+    soff[rb] = jr * (kWD / 8) + 8 * h;
   }
   f32x16 accm[kSRB], accq[kSRB];
 #pragma unroll
@@ -572,19 +591,25 @@ __global__ __launch_bounds__(64 * kSWaves, 2) void wide_scan_kernel(WScanParams 
   constexpr int NPL = PROD ? 4 : 2;            // query planes
   constexpr int QS = 72;                       // halves per LDS row (64 + 8 pad)
   __shared__ __align__(16) _Float16 s_q[2][NPL][32][QS];
-  const _Float16* planes[4] = {p.qh, p.ql, p.sh, p.sl};
   constexpr int QPIECES = NPL * 32 * 8 / (64 * kSWaves);   // 16-byte pieces per thread
+  static_assert(QPIECES == NPL && 64 * kSWaves == 256, "thread t loads piece t of every plane");
+  // Buffer descriptors over the workgroup's 32 query rows of each plane
+  // (rows past n_q read as zero): thread t loads the 16-byte piece t % 8 of
+  // row t / 8 of each plane, at the same 32-bit offset in all of them.
+  const uint32_t qrows = (uint32_t)(p.n_q - qb * 32 < 32 ? p.n_q - qb * 32 : 32);
+  const _Float16* planes[4] = {p.qh, p.ql, p.sh, p.sl};
+  __amdgpu_buffer_rsrc_t rq[NPL];
+#pragma unroll
+  for (int pl = 0; pl < NPL; ++pl)
+    rq[pl] = __builtin_amdgcn_make_buffer_rsrc((void*)(planes[pl] + qb * 32 * kWD), (short)0,
+                                               (int)(qrows * kWD * 2), kRsrcWord3);
+  const uint32_t qoff = (uint32_t)((((tid >> 3) & 31) * kWD + 64 * ((tid & 7) >> 2) + 8 * (tid & 3)) * 2);
   u32x4 qr[QPIECES];
   auto gload_q = [&](int hc) {
     const int c = hc >> 1, hh = hc & 1;
 #pragma unroll
-    for (int u = 0; u < QPIECES; ++u) {
-      const int t = tid + u * 64 * kSWaves;
-      const int pl = t >> 8, row = (t >> 3) & 31, j = t & 7;
-      const int64_t qa2 = qb * 32 + row;
-      const _Float16* src = planes[pl] + (qa2 < p.n_q ? qa2 : 0) * kWD + 128 * c + 64 * (j >> 2) + 32 * hh + 8 * (j & 3);
-      qr[u] = *reinterpret_cast<const u32x4*>(src);
-    }
+    for (int pl = 0; pl < NPL; ++pl)
+      qr[pl] = __builtin_amdgcn_raw_buffer_load_b128(rq[pl], qoff, (128 * c + 32 * hh) * 2, 0);
   };
   auto lstore_q = [&](int bf) {
 #pragma unroll
@@ -600,10 +625,20 @@ __global__ __launch_bounds__(64 * kSWaves, 2) void wide_scan_kernel(WScanParams 
     const int c = hc >> 1, hh = hc & 1;
 #pragma unroll
     for (int rb = 0; rb < kSRB; ++rb) {
-      const uint32_t* src = reinterpret_cast<const uint32_t*>(crow[rb] + 16 * CB * c + 8 * CB * h + 4 * CB * hh);
-#pragma unroll
-      for (int u = 0; u < CB; ++u) cw[bf][rb][u] = src[u];
-      if constexpr (PROD) sw[bf][rb] = *reinterpret_cast<const uint32_t*>(srow[rb] + 16 * c + 8 * h + 4 * hh);
+      const uint32_t o = CB * soff[rb] + 16 * CB * c + 4 * CB * hh;
+      if constexpr (CB == 1) {
+        cw[bf][rb][0] = __builtin_amdgcn_raw_buffer_load_b32(rc, o, 0, 0);
+      } else if constexpr (CB == 2) {
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rc, o, 0, 0);
+        cw[bf][rb][0] = v[0]; cw[bf][rb][1] = v[1];
+      } else if constexpr (CB == 3) {
+        const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(rc, o, 0, 0);
+        cw[bf][rb][0] = v[0]; cw[bf][rb][1] = v[1]; cw[bf][rb][2] = v[2];
+      } else {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rc, o, 0, 0);
+        cw[bf][rb][0] = v[0]; cw[bf][rb][1] = v[1]; cw[bf][rb][2] = v[2]; cw[bf][rb][3] = v[3];
+      }
+      if constexpr (PROD) sw[bf][rb] = __builtin_amdgcn_raw_buffer_load_b32(rs, soff[rb] + 16 * c + 4 * hh, 0, 0);
     }
   };
   auto compute = [&](int s, int bf) {
