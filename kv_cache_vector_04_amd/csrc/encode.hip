@@ -553,20 +553,25 @@ __device__ __forceinline__ float cross_max(float v) {
 // non-finite norm (inf, or NaN when an element is NaN).  Both lanes of a
 // pair see the same sums and take the same branches.
 template <int D>
-__device__ __forceinline__ float f32_rotate_half(const EncodeParams& p, const uint4* fmask, int64_t row,
-                                                 bool valid, float sgn, float (&x)[D / 2], float& pre_inv) {
+__device__ __forceinline__ float f32_rotate_half(const EncodeParams& p, const uint4* fmask, int64_t tile,
+                                                 float sgn, float (&x)[D / 2], float& pre_inv) {
   constexpr int HALF = D / 2;
-  const int h = (threadIdx.x & 63) >> 5;
-  if (valid) {
-    const float4* src = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p.x) + row * p.x_stride + h * HALF);
+  typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+  const int lane = threadIdx.x & 63, h = lane >> 5;
+  // a buffer descriptor over the (wave-uniform) tile's rows: rows past the
+  // end read as zeros
+  const int64_t r0 = tile * 32;
+  const int64_t left = p.n_rows - r0;
+  const uint32_t rows = left <= 0 ? 0u : (left < 32 ? (uint32_t)left : 32u);
+  const float* base = reinterpret_cast<const float*>(p.x) + (left > 0 ? r0 * p.x_stride : 0);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)base, (short)0, (int)(rows * (uint32_t)p.x_stride * 4u), 0x00020000);
+  const uint32_t off = ((uint32_t)(lane & 31) * (uint32_t)p.x_stride + (uint32_t)(h * HALF)) * 4u;
 #pragma unroll
-    for (int j = 0; j < HALF / 4; ++j) {
-      const float4 v = src[j];
-      x[4 * j] = v.x; x[4 * j + 1] = v.y; x[4 * j + 2] = v.z; x[4 * j + 3] = v.w;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < HALF; ++i) x[i] = 0.f;
+  for (int j = 0; j < HALF / 4; ++j) {
+    const u4v v = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16u * j, 0, 0);
+    x[4 * j] = __uint_as_float(v[0]); x[4 * j + 1] = __uint_as_float(v[1]);
+    x[4 * j + 2] = __uint_as_float(v[2]); x[4 * j + 3] = __uint_as_float(v[3]);
   }
   float nu2 = cross_sum(sum_squares<HALF>(x));
   pre_inv = 1.f;
@@ -618,22 +623,25 @@ __device__ __forceinline__ float f32_rotate_half(const EncodeParams& p, const ui
   return sqrtf(nu2);
 }
 
-// Loads the input of tile t for this lane (rows past the end read as zeros).
+// Loads the fp16 input of tile t for this lane through a buffer descriptor
+// over the tile's rows: 32-bit offsets, and rows past the end (or a tile
+// past the end) read as zeros with no branch.  t is wave-uniform.
 template <int D>
 __device__ __forceinline__ void half_load(const EncodeParams& p, int64_t t, uint32_t (&dst)[D / 4]) {
   constexpr int NP = D / 4;
+  typedef uint32_t u4v __attribute__((ext_vector_type(4)));
   const int lane = threadIdx.x & 63, h = lane >> 5;
-  const int64_t r = t * 32 + (lane & 31);
-  if (t < (p.n_rows + 31) / 32 && r < p.n_rows) {
-    const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const _Float16*>(p.x) + r * p.x_stride + h * (D / 2));
+  const int64_t r0 = t * 32;
+  const int64_t left = p.n_rows - r0;
+  const uint32_t rows = left <= 0 ? 0u : (left < 32 ? (uint32_t)left : 32u);
+  const _Float16* base = reinterpret_cast<const _Float16*>(p.x) + (left > 0 ? r0 * p.x_stride : 0);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)base, (short)0, (int)(rows * (uint32_t)p.x_stride * 2u), 0x00020000);
+  const uint32_t off = ((uint32_t)(lane & 31) * (uint32_t)p.x_stride + (uint32_t)(h * (D / 2))) * 2u;
 #pragma unroll
-    for (int j = 0; j < NP / 4; ++j) {
-      const uint4 v = src[j];
-      dst[4 * j] = v.x; dst[4 * j + 1] = v.y; dst[4 * j + 2] = v.z; dst[4 * j + 3] = v.w;
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < NP; ++j) dst[j] = 0u;
+  for (int j = 0; j < NP / 4; ++j) {
+    const u4v v = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16u * j, 0, 0);
+    dst[4 * j] = v[0]; dst[4 * j + 1] = v[1]; dst[4 * j + 2] = v[2]; dst[4 * j + 3] = v[3];
   }
 }
 
@@ -659,7 +667,6 @@ __device__ __forceinline__ void half_tiles(const EncodeParams& p, const HalfTabl
   const int h = lane >> 5;
   const float sgn = h ? -1.f : 1.f;
   const int64_t ntiles = (p.n_rows + 31) / 32;
-  const _Float16* __restrict__ xin = reinterpret_cast<const _Float16*>(p.x);
   const float lut_a = p.lut_a, lut_b = p.lut_b;
   const float cscale = PROD ? 256.f : 1.f;
   auto load_tile = [&](int64_t t, uint32_t (&dst)[NP]) { half_load<D>(p, t, dst); };
@@ -671,23 +678,15 @@ __device__ __forceinline__ void half_tiles(const EncodeParams& p, const HalfTabl
     if constexpr (F32IN) {
       // x may come back scaled by a power of two (nu_s is its norm)
       float pre_inv;
-      nu_s = f32_rotate_half<D>(p, T.fmask, row, valid, sgn, x, pre_inv);
+      nu_s = f32_rotate_half<D>(p, T.fmask, tile, sgn, x, pre_inv);
       nu_out = nu_s * pre_inv;
     } else {
     uint32_t u[NP];
     if (PF) {
 #pragma unroll
       for (int j = 0; j < NP; ++j) u[j] = nxt[j];
-    } else if (valid) {
-      const uint4* src = reinterpret_cast<const uint4*>(xin + row * p.x_stride + h * HALF);
-#pragma unroll
-      for (int j = 0; j < NP / 4; ++j) {
-        const uint4 v = src[j];
-        u[4 * j] = v.x; u[4 * j + 1] = v.y; u[4 * j + 2] = v.z; u[4 * j + 3] = v.w;
-      }
     } else {
-#pragma unroll
-      for (int j = 0; j < NP; ++j) u[j] = 0u;
+      half_load<D>(p, tile, u);
     }
     typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
     float acc[8];
@@ -807,6 +806,42 @@ __device__ __forceinline__ void half_tiles(const EncodeParams& p, const HalfTabl
     } else {
       uint32_t bh[KS][4], bl[KS][4];
       float g2[2] = {0.f, 0.f};
+      // S r' on the matrix cores, two 32-row tiles of S (mp) at a time: the
+      // six products of step ks (S_hi r_hi + S_hi r_lo + S_lo r_hi for both
+      // tiles)
+      auto project = [&](int mp, int ks, f32x16& c0, f32x16& c1) {
+        const int f0 = (2 * mp) * KS + ks, f1 = (2 * mp + 1) * KS + ks;
+        const half8_t a0h = __builtin_bit_cast(half8_t, T.frag[(2 * f0) * kWave + lane]);
+        const half8_t a0l = __builtin_bit_cast(half8_t, T.frag[(2 * f0 + 1) * kWave + lane]);
+        const half8_t a1h = __builtin_bit_cast(half8_t, T.frag[(2 * f1) * kWave + lane]);
+        const half8_t a1l = __builtin_bit_cast(half8_t, T.frag[(2 * f1 + 1) * kWave + lane]);
+        const half8_t rh = __builtin_bit_cast(half8_t, make_uint4(bh[ks][0], bh[ks][1], bh[ks][2], bh[ks][3]));
+        const half8_t rl = __builtin_bit_cast(half8_t, make_uint4(bl[ks][0], bl[ks][1], bl[ks][2], bl[ks][3]));
+        c0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0h, rh, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1h, rh, c1, 0, 0, 0);
+        c0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0h, rl, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1h, rl, c1, 0, 0, 0);
+        c0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0l, rh, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1l, rh, c1, 0, 0, 0);
+      };
+      // register v of lane half h holds row 16 h + v of the tile; bit =
+      // [p >= 0] (a result of exactly -0 reads as negative; it needs r = 0)
+      auto sign_words = [&](const f32x16& c0, const f32x16& c1, uint32_t& s0, uint32_t& s1) {
+        uint32_t w0 = 0u, w1 = 0u;
+#pragma unroll
+        for (int v = 15; v >= 0; --v) {
+          w0 = __builtin_amdgcn_alignbit(w0, __float_as_uint(c0[v]), 31);
+          w1 = __builtin_amdgcn_alignbit(w1, __float_as_uint(c1[v]), 31);
+        }
+        w0 = (w0 ^ 0xFFFFu) << (16 * h);
+        w1 = (w1 ^ 0xFFFFu) << (16 * h);
+        uint32_t a0 = w0, b0 = w0, a1 = w1, b1 = w1;
+        swap_halves(a0, b0);
+        swap_halves(a1, b1);
+        s0 = a0 | b0;
+        s1 = a1 | b1;
+      };
+      uint32_t sw[MT];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         float r[8];
@@ -833,46 +868,21 @@ __device__ __forceinline__ void half_tiles(const EncodeParams& p, const HalfTabl
       const float gamma2 = cross_sum(g2[0] + g2[1]);
       if (valid && h == 0) p.rnorm[row] = sqrtf(gamma2) * (1.f / 256.f);
 
-      // S r' on the matrix cores, two 32-row tiles of S at a time
-      uint32_t sw[MT];
 #pragma unroll 1
       for (int mp = 0; mp < MT / 2; ++mp) {
         f32x16 c0 = {}, c1 = {};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const int f0 = (2 * mp) * KS + ks, f1 = (2 * mp + 1) * KS + ks;
-          const half8_t a0h = __builtin_bit_cast(half8_t, T.frag[(2 * f0) * kWave + lane]);
-          const half8_t a0l = __builtin_bit_cast(half8_t, T.frag[(2 * f0 + 1) * kWave + lane]);
-          const half8_t a1h = __builtin_bit_cast(half8_t, T.frag[(2 * f1) * kWave + lane]);
-          const half8_t a1l = __builtin_bit_cast(half8_t, T.frag[(2 * f1 + 1) * kWave + lane]);
-          const half8_t rh = __builtin_bit_cast(half8_t, make_uint4(bh[ks][0], bh[ks][1], bh[ks][2], bh[ks][3]));
-          const half8_t rl = __builtin_bit_cast(half8_t, make_uint4(bl[ks][0], bl[ks][1], bl[ks][2], bl[ks][3]));
-          c0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0h, rh, c0, 0, 0, 0);
-          c1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1h, rh, c1, 0, 0, 0);
-          c0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0h, rl, c0, 0, 0, 0);
-          c1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1h, rl, c1, 0, 0, 0);
-          c0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0l, rh, c0, 0, 0, 0);
-          c1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1l, rh, c1, 0, 0, 0);
+          project(mp, ks, c0, c1);
           __builtin_amdgcn_sched_barrier(0);
         }
-        // register v of lane half h holds row 16 h + v of the tile; bit =
-        // [p >= 0] (a result of exactly -0 reads as negative; it needs r = 0)
-        uint32_t w0 = 0u, w1 = 0u;
-#pragma unroll
-        for (int v = 15; v >= 0; --v) {
-          w0 = __builtin_amdgcn_alignbit(w0, __float_as_uint(c0[v]), 31);
-          w1 = __builtin_amdgcn_alignbit(w1, __float_as_uint(c1[v]), 31);
-        }
-        w0 = (w0 ^ 0xFFFFu) << (16 * h);
-        w1 = (w1 ^ 0xFFFFu) << (16 * h);
-        uint32_t a0 = w0, b0 = w0, a1 = w1, b1 = w1;
-        swap_halves(a0, b0);
-        swap_halves(a1, b1);
+        uint32_t s0, s1;
+        sign_words(c0, c1, s0, s1);
 #pragma unroll
         for (int t = 0; t < MT / 2; ++t) {
           if (t == mp) {
-            sw[2 * t] = a0 | b0;
-            sw[2 * t + 1] = a1 | b1;
+            sw[2 * t] = s0;
+            sw[2 * t + 1] = s1;
           }
         }
       }
@@ -897,7 +907,7 @@ __global__ __launch_bounds__((HalfLaunch<PROD, F32IN>::kWaves * kWave), (HalfLau
   const int tid = threadIdx.x;
   const EncodeParams* kp = (const EncodeParams*)__builtin_amdgcn_kernarg_segment_ptr();
   const int64_t tstride = (int64_t)gridDim.x * kHalfWaves;
-  const int64_t tile = (int64_t)blockIdx.x * kHalfWaves + (tid >> 6);
+  const int64_t tile = (int64_t)blockIdx.x * kHalfWaves + __builtin_amdgcn_readfirstlane(tid >> 6);
   uint32_t nxt[D / 4];
   // the first tile's input is in flight during the set-up
   if (PF) half_load<D>(p, tile, nxt);
@@ -928,7 +938,7 @@ template <int D, int CBK, int CBV>
 __global__ __launch_bounds__((kKVKeyWaves + kKVValWaves) * kWave, 3) void encode_kv_half_kernel(EncodeKVParams pp) {
   __shared__ HalfTables<D, CBK, true, kKVRotK> TK;
   __shared__ HalfTables<D, CBV, false, kKVRotV> TV;
-  const int tid = threadIdx.x, wave = tid >> 6;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const EncodeKVParams* kpp = (const EncodeKVParams*)__builtin_amdgcn_kernarg_segment_ptr();
   const bool key_wave = wave < kKVKeyWaves;
   const int64_t vtile = (int64_t)blockIdx.x * kKVValWaves + (wave - kKVKeyWaves);
@@ -1057,6 +1067,8 @@ static bool fill_params(const tq_codec& c, const void* x, int64_t n_rows, const 
   p = {};
   p.x = x;
   p.x_stride = x_stride > 0 ? x_stride : c.d;
+  // the two-lanes-per-vector kernels address a 32-row tile with 32-bit offsets
+  if (p.x_stride > (int64_t)1 << 24) return false;
   p.n_rows = n_rows;
   p.idx = out.idx;
   p.qjl = out.qjl;
