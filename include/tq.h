@@ -151,6 +151,8 @@ typedef struct tq_rope {
  *             256-byte aligned; may be NULL when that size is 0 (it is 0
  *             for d = 64 and 128 and for TQ_MSE).  Contents need no
  *             initialisation; calls sharing it must not overlap in time.
+ * n_rows = 0 checks the codecs and returns TQ_OK without reading any
+ * pointer (k, v, the planes and workspace may then be NULL).
  * Returns TQ_OK, TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_WORKSPACE or
  * TQ_ERR_HIP. */
 size_t tq_encode_kv_workspace(const tq_codec* kc, const tq_codec* vc, int64_t n_rows);
@@ -172,6 +174,8 @@ int tq_encode_kv(const tq_codec* kc, const tq_codec* vc, const void* k,
  *   in    host struct of device planes holding n_rows rows
  *   out   device [n_rows][d] of out_dtype (TQ_F16, rounded toward zero, or
  *         TQ_F32), 16-byte aligned; written only
+ * n_rows = 0 checks the codec and returns TQ_OK; `in` and `out` may then be
+ * NULL.
  * Returns TQ_OK, TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED or TQ_ERR_HIP. */
 int tq_decode_kv(const tq_codec* c, const tq_packed* in, int64_t n_rows, void* out,
                  int out_dtype, tq_stream_t stream);
@@ -210,8 +214,9 @@ int tq_outlier_order(const float* x, int64_t n_rows, int d, int d_hi, int32_t* o
  *   k, v        device, n_rows x 128 of `dtype` (TQ_F16 or TQ_F32), 16-byte aligned
  *   kout, vout  arrays of two tq_packed: the hi half's planes, then the lo
  *               half's, each sized for its own codec as for tq_encode_kv
- * No RoPE and no workspace.  Returns TQ_OK, TQ_ERR_INVALID_ARG,
- * TQ_ERR_UNSUPPORTED (halves other than 64 + 64) or TQ_ERR_HIP. */
+ * No RoPE and no workspace.  n_rows = 0 checks the codecs only (pointers may
+ * be NULL).  Returns TQ_OK, TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED (halves
+ * other than 64 + 64) or TQ_ERR_HIP. */
 int tq_encode_split(const tq_split_codec* kc, const tq_split_codec* vc, const void* k,
                     const void* v, int dtype, int64_t n_rows, const tq_packed* kout,
                     const tq_packed* vout, tq_stream_t stream);
@@ -219,7 +224,7 @@ int tq_encode_split(const tq_split_codec* kc, const tq_split_codec* vc, const vo
 /* Decode one tensor's two halves (in[0]: hi, in[1]: lo) into rows of
  * hi.d + lo.d elements of out_dtype (TQ_F16, rounded toward zero, or
  * TQ_F32) at `out` (device, 16-byte aligned), as tq_decode_kv does for
- * each half. */
+ * each half; n_rows = 0 checks the codec only. */
 int tq_decode_split(const tq_split_codec* c, const tq_packed* in, int64_t n_rows, void* out,
                     int out_dtype, tq_stream_t stream);
 
@@ -289,14 +294,16 @@ int tq_vq_search_build(const tq_vq_codec* c, void* table, size_t bytes);
  *   x     device, n_rows x d of `dtype` (TQ_F16 or TQ_F32), 16-byte aligned
  *   idx   device, n_rows x (d/2) log2(N) / 8 bytes, 4-byte aligned (output)
  *   norm  device, n_rows floats (output)
- * d = 64 or 128 (other d: TQ_ERR_UNSUPPORTED).  Returns TQ_OK,
- * TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED or TQ_ERR_HIP. */
+ * d = 64 or 128 (other d: TQ_ERR_UNSUPPORTED).  n_rows = 0 checks the codec
+ * only (pointers may be NULL).  Returns TQ_OK, TQ_ERR_INVALID_ARG,
+ * TQ_ERR_UNSUPPORTED or TQ_ERR_HIP. */
 int tq_encode_vq(const tq_vq_codec* c, const void* x, int dtype, int64_t n_rows,
                  uint8_t* idx, float* norm, tq_stream_t stream);
 
 /* Decode: x_hat = nu * Pi^T (codewords of the row's blocks, concatenated),
  * written as n_rows x d of out_dtype (TQ_F16 rounded toward zero, or
- * TQ_F32) to `out` (device, 16-byte aligned). */
+ * TQ_F32) to `out` (device, 16-byte aligned); n_rows = 0 checks the codec
+ * only. */
 int tq_decode_vq(const tq_vq_codec* c, const uint8_t* idx, const float* norm, int64_t n_rows,
                  void* out, int out_dtype, tq_stream_t stream);
 

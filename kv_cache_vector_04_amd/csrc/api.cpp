@@ -98,12 +98,17 @@ extern "C" int tq_encode_kv(const tq_codec* kc, const tq_codec* vc, const void* 
   const tq_packed* outs[2] = {kout, vout};
   for (int s = 0; s < 2; ++s) {
     if (cs[s] == nullptr) continue;
-    int st = check_codec(cs[s]);
+    const int st = check_codec(cs[s]);
     if (st != TQ_OK) return st;
-    if ((st = check_planes(cs[s], outs[s])) != TQ_OK) return st;
+  }
+  // zero rows: nothing to read or write, so no pointer needs to be valid
+  if (n_rows == 0) return TQ_OK;
+  for (int s = 0; s < 2; ++s) {
+    if (cs[s] == nullptr) continue;
+    const int st = check_planes(cs[s], outs[s]);
+    if (st != TQ_OK) return st;
     if (xs[s] == nullptr || !aligned(xs[s], 16)) return TQ_ERR_INVALID_ARG;
   }
-  if (n_rows == 0) return TQ_OK;
   const size_t need = encode_need(kc, vc, n_rows);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256)))
     return TQ_ERR_WORKSPACE;
@@ -124,9 +129,10 @@ extern "C" int tq_decode_kv(const tq_codec* c, const tq_packed* in, int64_t n_ro
   int st = check_codec(c);
   if (st != TQ_OK) return st;
   if (c->d != 64 && c->d != 128) return TQ_ERR_UNSUPPORTED;
-  if ((st = check_planes(c, in)) != TQ_OK) return st;
   if (n_rows < 0 || (out_dtype != TQ_F16 && out_dtype != TQ_F32)) return TQ_ERR_INVALID_ARG;
+  // zero rows: nothing to read or write, so no pointer needs to be valid
   if (n_rows == 0) return TQ_OK;
+  if ((st = check_planes(c, in)) != TQ_OK) return st;
   if (out == nullptr || !aligned(out, 16)) return TQ_ERR_INVALID_ARG;
   return hip_status(tqk::launch_materialize(*c, *in, n_rows, out, out_dtype,
                                             reinterpret_cast<hipStream_t>(stream)));
@@ -135,11 +141,16 @@ extern "C" int tq_decode_kv(const tq_codec* c, const tq_packed* in, int64_t n_ro
 namespace {
 
 // both halves 64 wide: the split of a 128-channel row
-int check_split(const tq_split_codec* c, const tq_packed* planes) {
+int check_split_codec(const tq_split_codec* c) {
   int st = check_codec(&c->hi);
   if (st != TQ_OK) return st;
   if ((st = check_codec(&c->lo)) != TQ_OK) return st;
-  if (c->hi.d != 64 || c->lo.d != 64) return TQ_ERR_UNSUPPORTED;
+  return c->hi.d != 64 || c->lo.d != 64 ? TQ_ERR_UNSUPPORTED : TQ_OK;
+}
+
+int check_split(const tq_split_codec* c, const tq_packed* planes) {
+  int st = check_split_codec(c);
+  if (st != TQ_OK) return st;
   if (planes == nullptr) return TQ_ERR_INVALID_ARG;
   if ((st = check_planes(&c->hi, &planes[0])) != TQ_OK) return st;
   return check_planes(&c->lo, &planes[1]);
@@ -155,13 +166,21 @@ extern "C" int tq_encode_split(const tq_split_codec* kc, const tq_split_codec* v
   const tq_split_codec* cs[2] = {kc, vc};
   const void* xs[2] = {k, v};
   const tq_packed* outs[2] = {kout, vout};
+  if (n_rows == 0) {
+    // zero rows: the codecs must still be valid, no pointer is read
+    for (int s = 0; s < 2; ++s) {
+      if (cs[s] == nullptr) continue;
+      const int st = check_split_codec(cs[s]);
+      if (st != TQ_OK) return st;
+    }
+    return TQ_OK;
+  }
   for (int s = 0; s < 2; ++s) {
     if (cs[s] == nullptr) continue;
     const int st = check_split(cs[s], outs[s]);
     if (st != TQ_OK) return st;
     if (xs[s] == nullptr || !aligned(xs[s], 16)) return TQ_ERR_INVALID_ARG;
   }
-  if (n_rows == 0) return TQ_OK;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   const int64_t stride = 128;
   const size_t esize = dtype == TQ_F16 ? 2 : 4;
@@ -191,10 +210,12 @@ extern "C" int tq_encode_split(const tq_split_codec* kc, const tq_split_codec* v
 extern "C" int tq_decode_split(const tq_split_codec* c, const tq_packed* in, int64_t n_rows,
                                void* out, int out_dtype, tq_stream_t stream) {
   if (c == nullptr) return TQ_ERR_INVALID_ARG;
-  int st = check_split(c, in);
+  int st = check_split_codec(c);
   if (st != TQ_OK) return st;
   if (n_rows < 0 || (out_dtype != TQ_F16 && out_dtype != TQ_F32)) return TQ_ERR_INVALID_ARG;
+  // zero rows: nothing to read or write, so no pointer needs to be valid
   if (n_rows == 0) return TQ_OK;
+  if ((st = check_split(c, in)) != TQ_OK) return st;
   if (out == nullptr || !aligned(out, 16)) return TQ_ERR_INVALID_ARG;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   const size_t esize = out_dtype == TQ_F16 ? 2 : 4;

@@ -129,6 +129,32 @@ def test_decode_validation_before_launch(L):
     assert dec(ctypes.byref(wide), ctypes.byref(pv), 10, fake, tq.TQ_F16, None) == tq.TQ_ERR_UNSUPPORTED
 
 
+def test_zero_rows_need_no_pointers(L):
+    """n_rows = 0 checks the codecs and returns before any pointer is read, so
+    an empty batch needs no buffers at all."""
+    kc = _codec_struct(L, 128, tq.TQ_PROD, 4)
+    vc = _codec_struct(L, 128, tq.TQ_MSE, 4)
+    K, V = ctypes.byref(kc), ctypes.byref(vc)
+    assert L.tq_encode_kv(K, V, None, None, tq.TQ_F16, 0, None, None, None, None, 0, None) == tq.TQ_OK
+    assert L.tq_decode_kv(K, None, 0, None, tq.TQ_F16, None) == tq.TQ_OK
+    # an invalid codec or argument is still reported at zero rows
+    bad = _codec_struct(L, 128, tq.TQ_MSE, 4)
+    bad.bits = 9
+    assert L.tq_encode_kv(ctypes.byref(bad), None, None, None, tq.TQ_F16, 0, None, None, None, None,
+                          0, None) != tq.TQ_OK
+    assert L.tq_encode_kv(K, V, None, None, 7, 0, None, None, None, None, 0, None) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_decode_kv(K, None, 0, None, 7, None) == tq.TQ_ERR_INVALID_ARG
+    sk = tq.TQSplitCodec(_codec_struct(L, 64, tq.TQ_PROD, 3), _codec_struct(L, 64, tq.TQ_PROD, 2))
+    sv = tq.TQSplitCodec(_codec_struct(L, 64, tq.TQ_MSE, 3), _codec_struct(L, 64, tq.TQ_MSE, 2))
+    assert L.tq_encode_split(ctypes.byref(sk), ctypes.byref(sv), None, None, tq.TQ_F16, 0, None, None,
+                             None) == tq.TQ_OK
+    assert L.tq_decode_split(ctypes.byref(sv), None, 0, None, tq.TQ_F32, None) == tq.TQ_OK
+    wide = tq.TQSplitCodec(kc, kc)   # halves of 128: no split kernel
+    assert L.tq_encode_split(ctypes.byref(wide), None, None, None, tq.TQ_F16, 0, None, None,
+                             None) == tq.TQ_ERR_UNSUPPORTED
+    assert L.tq_decode_split(ctypes.byref(wide), None, 0, None, tq.TQ_F32, None) == tq.TQ_ERR_UNSUPPORTED
+
+
 @pytest.mark.parametrize("d,n", [(6, 2), (64, 2), (64, 8), (64, 32), (128, 4), (128, 16), (128, 64)])
 def test_library_vq_codebook_matches_oracle(L, d, n):
     from oracle import fibquant_codebook

@@ -104,3 +104,19 @@ def test_split_attention_rejects_scores_buffer(setup):
                           scores_out=torch.empty((1, hq, 1, ctx), device="cuda"))
     torch.cuda.synchronize()
     assert torch.isfinite(out).all()
+
+
+def test_empty_batches_are_no_ops(setup):
+    """Zero rows: encode and decode return empty results without a launch,
+    and leave the existing codes untouched."""
+    say("validation: zero-row encode / decode")
+    s = setup
+    d = s["d"]
+    before = s["kp"].idx.clone()
+    k0 = torch.empty((0, d), dtype=torch.float16, device="cuda")
+    kp, vp = tq.encode_kv(s["kc"], s["vc"], k0, k0.clone())
+    assert kp.n == 0 and vp.n == 0 and kp.idx.shape == (0, d * 3 // 8)
+    assert tq.decode_kv(s["kc"], kp, 0).shape == (0, d)
+    assert tq.decode_kv(s["vc"], s["vp"], 0, dtype=torch.float32).shape == (0, d)
+    torch.cuda.synchronize()
+    assert torch.equal(before, s["kp"].idx)
