@@ -590,13 +590,57 @@ struct MergeParams {
 
 // Log-sum-exp merge of the token ranges of one query row, then
 // o = D_V * (H a) / sqrt(d) (for a split codec H is H_64 on each half).
+// Thread i owns coordinate i.  A pass over kMergeBatch records issues all of
+// its loads before it waits (one memory round trip): each thread's value of
+// every record, and in lane u of each wave the (max, sum) pair of record u,
+// whose weight the other lanes then read from that lane.  The butterflies
+// run inside the wave (DPP and lane swaps); only the stage across the two
+// waves of d = 128 goes through LDS.
+constexpr int kMergeBatch = 32;
+
+// One butterfly stage of stride hh < 64 inside the wave: the lane with
+// bit hh of its index clear keeps x + x', the other x' - x (x' the
+// partner's value, the partner's index lower).
+__device__ __forceinline__ float wave_butterfly(float x, int lane, int hh) {
+  switch (hh) {
+    case 1: {
+      const float o = dpp_f<0xB1>(x);            // quad_perm [1, 0, 3, 2]
+      return (lane & 1) ? (o - x) : (x + o);
+    }
+    case 2: {
+      const float o = dpp_f<0x4E>(x);            // quad_perm [2, 3, 0, 1]
+      return (lane & 2) ? (o - x) : (x + o);
+    }
+    case 4: {
+      // row_ror 4 reads lane l - 4 of the row, row_ror 12 lane l + 4
+      const float lo = dpp_f<0x124>(x), hi = dpp_f<0x12C>(x);
+      return (lane & 4) ? (lo - x) : (x + hi);
+    }
+    case 8: {
+      const float o = dpp_f<0x128>(x);           // row_ror 8: lane l ^ 8
+      return (lane & 8) ? (o - x) : (x + o);
+    }
+    case 16: {
+      // [0]: the value of the lower row of the pair, [1]: of the upper row
+      const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+      const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+      return (lane & 16) ? (a - b) : (a + b);
+    }
+    default: {
+      // [0]: the value of the lower half, [1]: of the upper half
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+      const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+      return (lane & 32) ? (a - b) : (a + b);
+    }
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(D) void merge_kernel(MergeParams p) {
   constexpr int REC = D + 2;
-  constexpr int CH = 2 * D < 128 ? 2 * D : 128;  // (max, sum) pairs staged per pass
+  constexpr int NB = kMergeBatch;
   __shared__ float s_v[D];
-  __shared__ float s_ml[CH];
-  const int i = threadIdx.x;
+  const int i = threadIdx.x, lane = i & 63;
   const int64_t row = blockIdx.x;                 // (b, h, a)
   const int a = (int)(row % p.n_q);
   const int64_t bh = row / p.n_q;
@@ -609,44 +653,37 @@ __global__ __launch_bounds__(D) void merge_kernel(MergeParams p) {
   const float* base = p.part + (bgc * p.splits * kDecRows + r) * REC;
   const int64_t stride = (int64_t)kDecRows * REC;
   float M = -INFINITY, L = 0.f, v = 0.f;
-  for (int s0 = 0; s0 < p.splits; s0 += CH / 2) {
-    const int ns = (p.splits - s0) < CH / 2 ? (p.splits - s0) : CH / 2;
-    __syncthreads();
-    for (int t = i; t < 2 * ns; t += D) s_ml[t] = base[(s0 + (t >> 1)) * stride + D + (t & 1)];
-    __syncthreads();
-    float Mc = M;
-    for (int s = 0; s < ns; ++s) Mc = fmaxf(Mc, s_ml[2 * s]);
+  for (int s0 = 0; s0 < p.splits; s0 += NB) {
+    const int ns = (p.splits - s0) < NB ? (p.splits - s0) : NB;
+    // records past the last one re-read the last (and are weighted 0)
+    float x[NB];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) x[u] = base[(int64_t)(s0 + (u < ns ? u : ns - 1)) * stride + i];
+    const float* mine = base + (int64_t)(s0 + (lane < ns ? lane : ns - 1)) * stride;
+    float mu = mine[D], lu = mine[D + 1];
+    if (lane >= ns) {
+      mu = -INFINITY;
+      lu = 0.f;
+    }
+    const float Mc = fmaxf(M, wave_max(mu));
+    const float f = mu == -INFINITY ? 0.f : __expf(mu - Mc);
     const float rescale = M == -INFINITY ? 0.f : __expf(M - Mc);
-    L *= rescale;
+    L = fmaf(L, rescale, wave_sum(lu * f));
     v *= rescale;
-    int s = 0;
-    for (; s + 32 <= ns; s += 32) {
-      float x[32];     // all loads of the chunk in flight together
 #pragma unroll
-      for (int u = 0; u < 32; ++u) x[u] = base[(s0 + s + u) * stride + i];
-#pragma unroll
-      for (int u = 0; u < 32; ++u) {
-        const float ms = s_ml[2 * (s + u)];
-        const float f = ms == -INFINITY ? 0.f : __expf(ms - Mc);
-        v = fmaf(x[u], f, v);
-        L = fmaf(s_ml[2 * (s + u) + 1], f, L);
-      }
-    }
-    for (; s < ns; ++s) {
-      const float ms = s_ml[2 * s];
-      const float f = ms == -INFINITY ? 0.f : __expf(ms - Mc);
-      v = fmaf(base[(s0 + s) * stride + i], f, v);
-      L = fmaf(s_ml[2 * s + 1], f, L);
-    }
+    for (int u = 0; u < NB; ++u)
+      v = fmaf(x[u], __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), u)), v);
     M = Mc;
   }
   v /= L;
-  for (int hh = 1; hh < p.wht_len; hh <<= 1) {
-    __syncthreads();
+#pragma unroll
+  for (int hh = 1; hh < (D < 64 ? D : 64); hh <<= 1)
+    if (hh < p.wht_len) v = wave_butterfly(v, lane, hh);
+  if (D == 128 && p.wht_len == 128) {
     s_v[i] = v;
     __syncthreads();
-    const float o = s_v[i ^ hh];
-    v = (i & hh) ? (o - v) : (v + o);
+    const float o = s_v[i ^ 64];
+    v = (i & 64) ? (o - v) : (v + o);
   }
   const uint32_t bit = (p.vflip[i >> 5] >> (i & 31)) & 1u;
   v *= p.inv_sqrt_d;
