@@ -196,6 +196,7 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(MfmaDecodeArgs p) {
   __shared__ float s_F[kMRows], s_Gs[kMRows], s_T[kMRows], s_U[kMRows];
   __shared__ float s_ws[16];                   // per-wave max |S q'| and sum
   __shared__ float s_vc[16];
+  __shared__ float s_alpha[8];                 // key table in odd monomials
   __shared__ __align__(16) float s_wt[W * 64];   // per-wave weight transpose
 
   const int tid = threadIdx.x;
@@ -293,61 +294,80 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(MfmaDecodeArgs p) {
   };
 
   // ---- set-up ----
-  // Loads in the order they are needed: the query rows, the S rows of S q'
-  // (cached after the first workgroups), and only once the query rows are
-  // rotated, the first NBUF steps' codes, which stay in flight during the
-  // rest of the set-up.  (Issued at once, the codes of every workgroup would
-  // queue in front of the query rows.)  Each step refills its slot, NBUF
-  // steps ahead, once it is done with it.
+  // Loads in the order they are needed, none waited on before the next one
+  // is issued: the query rows (wave 0), the S rows of S q' (cached after the
+  // first workgroups), and only once the query rows are rotated, the first
+  // NBUF steps' codes, which stay in flight during the rest of the set-up.
+  // (Issued at once, the codes of every workgroup would queue in front of
+  // the query rows.)  Each step refills its slot, NBUF steps ahead, once it
+  // is done with it.  Kernel arguments read at a per-lane index would be
+  // memory loads on this chain: the code tables reach LDS through scalar
+  // reads instead.
   // Wave 0 rotates all four query rows: lane (row r = lane / 16, j = lane % 16)
   // holds coordinates 8 j .. 8 j + 7 of row r.
   const int qr = lane >> 4, qj = lane & 15;
-  float xq[8];
-#pragma unroll
-  for (int c = 0; c < 8; ++c) xq[c] = 0.f;
+  uint4 qraw0 = make_uint4(0u, 0u, 0u, 0u), qraw1 = qraw0;
   if (wave == 0 && qr < nrows) {
+    // the lane's 8 coordinates: 16 bytes of fp16 or 32 bytes of fp32
     const int64_t off = (row_base + qr) * D + 8 * qj;
-    if (p.q_f16) {
-      const uint4 v = *reinterpret_cast<const uint4*>(reinterpret_cast<const _Float16*>(p.q) + off);
-      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+    const uint4* src = reinterpret_cast<const uint4*>(static_cast<const char*>(p.q) + off * (p.q_f16 ? 2 : 4));
+    qraw0 = src[0];
+    qraw1 = src[p.q_f16 ? 0 : 1];   // (unused for fp16: a second read of the first 16 bytes)
+  }
+  const MfmaDecodeArgs* kp = (const MfmaDecodeArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+  // RoPE angles of the lane's four coordinate pairs, loaded beside the query
+  double th[4] = {0.0, 0.0, 0.0, 0.0};
+  if (wave == 0 && p.rope) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        xq[2 * c] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u[c] & 0xffffu));
-        xq[2 * c + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u[c] >> 16));
-      }
-    } else {
-      const float4* src = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p.q) + off);
-      const float4 v0 = src[0], v1 = src[1];
-      xq[0] = v0.x; xq[1] = v0.y; xq[2] = v0.z; xq[3] = v0.w;
-      xq[4] = v1.x; xq[5] = v1.y; xq[6] = v1.z; xq[7] = v1.w;
-    }
+    for (int c = 0; c < 4; ++c) th[c] = kp->theta[4 * qj + c];
   }
   // S rows for S q': thread -> (coordinate si, k-part sp)
+  // (with exactly KP D threads every thread loads: no branch, so the wait
+  // for the query rows does not also wait for these loads)
   const int si = tid % D, sp = tid / D;
-  const bool sq_thread = tid < KP * D;
+  const bool sq_thread = THREADS == KP * D || tid < KP * D;
   float4 srow[KL / 4];
   if (sq_thread) {
     const float4* S4 = reinterpret_cast<const float4*>(p.S + (size_t)si * D + sp * KL);
 #pragma unroll
     for (int j = 0; j < KL / 4; ++j) srow[j] = S4[j];
   }
-  const MfmaDecodeArgs* kp = (const MfmaDecodeArgs*)__builtin_amdgcn_kernarg_segment_ptr();
-  if (tid < 16) s_vc[tid] = kp->vcent[tid];
+  if (tid == 64) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s_vc[i] = p.vcent[i];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s_alpha[i] = p.alpha[i];
+  }
   if (wave == 0) {
-    float (&x)[8] = xq;
+    float x[8];
+    if (p.q_f16) {
+      const uint32_t u[4] = {qraw0.x, qraw0.y, qraw0.z, qraw0.w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        x[2 * c] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u[c] & 0xffffu));
+        x[2 * c + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u[c] >> 16));
+      }
+    } else {
+      x[0] = __uint_as_float(qraw0.x); x[1] = __uint_as_float(qraw0.y);
+      x[2] = __uint_as_float(qraw0.z); x[3] = __uint_as_float(qraw0.w);
+      x[4] = __uint_as_float(qraw1.x); x[5] = __uint_as_float(qraw1.y);
+      x[6] = __uint_as_float(qraw1.z); x[7] = __uint_as_float(qraw1.w);
+    }
     if (p.rope) {
       // interleaved pairs (2 p, 2 p + 1), p = 4 j + c
       const int64_t pos = (int64_t)p.pos0 + ((lr0 + qr) % p.n_q);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         float sn, cs;
-        sincos_reduced((double)pos * kp->theta[4 * qj + c], sn, cs);
+        sincos_reduced((double)pos * th[c], sn, cs);
         const float a0 = x[2 * c], b0 = x[2 * c + 1];
         x[2 * c] = a0 * cs - b0 * sn;
         x[2 * c + 1] = a0 * sn + b0 * cs;
       }
     }
-    const uint32_t fw = (kp->kflip[qj >> 2] >> (8 * (qj & 3))) & 0xffu;
+    const int fq = qj >> 2;
+    const uint32_t kfw = fq == 0 ? p.kflip[0] : (fq == 1 ? p.kflip[1] : (fq == 2 ? p.kflip[2] : p.kflip[3]));
+    const uint32_t fw = (kfw >> (8 * (qj & 3))) & 0xffu;
 #pragma unroll
     for (int c = 0; c < 8; ++c)
       x[c] = __uint_as_float(__float_as_uint(x[c]) ^ (((fw >> c) & 1u) << 31));
@@ -413,6 +433,58 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(MfmaDecodeArgs p) {
 #pragma unroll
   for (int k = 0; k < NBUF; ++k)
     if (wave + k * W < ng) load_step(wave + k * W, ring[k]);
+
+  // B operands: for product u, lane (g, n = 4 lam + r), dword s, byte e the
+  // limb lam of (2 coef x 2^-j) / F_r, where the byte pairs with bit j of
+  // byte e of the A dword (see the key-bit masks in the scan below).  One
+  // item t = (u, g, r, s, e) writes that byte of all four limb lanes.  The
+  // code-bit products need only q', so they are built while the S rows are
+  // still arriving; the QJL products follow S q'.
+  uint8_t* lb8 = reinterpret_cast<uint8_t*>(&s_lb[0][0]);
+  auto limb_item = [&](int t) {
+    const int e = t & 3, s = (t >> 2) & 3, r = (t >> 4) & 3, gg = (t >> 6) & 3, u = t >> 8;
+    int j, coord;
+    float x;
+    bool qjl = false;
+    if (u < NL) {
+      const int up = 4 * u + s, a = up >> 3;
+      j = up & 7;
+      const int P = 32 * a + 8 * e + j;
+      coord = 32 * gg + P / CBK;
+      x = s_alpha[P % CBK] * s_q[r][coord];
+    } else if (u < NL + NC) {
+      if constexpr (CBK == 3) {
+        j = 4 * (u - NL) + s;
+        const int P = 8 * e + j, a = P % 3;
+        coord = 32 * gg + (P + 32 * a) / 3;
+        x = s_alpha[3] * s_q[r][coord];
+      } else {
+        const int up = 4 * (u - NL) + s, a = up >> 3;
+        j = up & 7;
+        const int P = 8 * e + j;
+        coord = 32 * gg + 8 * a + (P >> 2);
+        x = s_alpha[4 + (P & 3)] * s_q[r][coord];
+      }
+    } else {
+      j = 4 * (u - NL - NC) + s;
+      coord = 32 * gg + 8 * e + j;
+      x = s_sq[r][coord];
+      qjl = true;
+    }
+    // the A byte of bit 7 reads as int8 -128: the sign moves into B
+    const float invF = qjl ? 1.f / limb_scale(2.f * fmaxf(s_ws[4 * r], s_ws[4 * r + 2])) : s_F[r];
+    const uint32_t l4 = limbs_of(ldexpf(j == 7 ? -2.f * x : 2.f * x, -j) * invF);
+#pragma unroll
+    for (int la = 0; la < 4; ++la)
+      lb8[(u * 64 + 16 * gg + 4 * la + r) * 16 + 4 * s + e] = (uint8_t)(l4 >> (8 * la));
+  };
+  constexpr int NKC = (NL + NC) * 256;   // items of the code-bit products
+#pragma unroll
+  for (int k = 0; k < (NKC + THREADS - 1) / THREADS; ++k) {
+    const int t = tid + k * THREADS;
+    if (t < NKC) limb_item(t);
+  }
+
   // S q' partial sums over this thread's k-part
   if (sq_thread) {
     float a[kMRows] = {0.f, 0.f, 0.f, 0.f};
@@ -447,48 +519,7 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(MfmaDecodeArgs p) {
     }
   }
   __syncthreads();
-  // B operands: for product u, lane (g, n = 4 lam + r), dword s, byte e the
-  // limb lam of (2 coef x 2^-j) / F_r, where the byte pairs with bit j of
-  // byte e of the A dword (see the key-bit masks in the scan below).  One
-  // thread per (u, g, r, s, e) writes that byte of all four limb lanes.
-  uint8_t* lb8 = reinterpret_cast<uint8_t*>(&s_lb[0][0]);
-  for (int t = tid; t < NM * 256; t += THREADS) {
-    const int e = t & 3, s = (t >> 2) & 3, r = (t >> 4) & 3, gg = (t >> 6) & 3, u = t >> 8;
-    int j, coord;
-    float x;
-    bool qjl = false;
-    if (u < NL) {
-      const int up = 4 * u + s, a = up >> 3;
-      j = up & 7;
-      const int P = 32 * a + 8 * e + j;
-      coord = 32 * gg + P / CBK;
-      x = kp->alpha[P % CBK] * s_q[r][coord];
-    } else if (u < NL + NC) {
-      if constexpr (CBK == 3) {
-        j = 4 * (u - NL) + s;
-        const int P = 8 * e + j, a = P % 3;
-        coord = 32 * gg + (P + 32 * a) / 3;
-        x = kp->alpha[3] * s_q[r][coord];
-      } else {
-        const int up = 4 * (u - NL) + s, a = up >> 3;
-        j = up & 7;
-        const int P = 8 * e + j;
-        coord = 32 * gg + 8 * a + (P >> 2);
-        x = kp->alpha[4 + (P & 3)] * s_q[r][coord];
-      }
-    } else {
-      j = 4 * (u - NL - NC) + s;
-      coord = 32 * gg + 8 * e + j;
-      x = s_sq[r][coord];
-      qjl = true;
-    }
-    // the A byte of bit 7 reads as int8 -128: the sign moves into B
-    const float invF = qjl ? 1.f / limb_scale(2.f * fmaxf(s_ws[4 * r], s_ws[4 * r + 2])) : s_F[r];
-    const uint32_t l4 = limbs_of(ldexpf(j == 7 ? -2.f * x : 2.f * x, -j) * invF);
-#pragma unroll
-    for (int la = 0; la < 4; ++la)
-      lb8[(u * 64 + 16 * gg + 4 * la + r) * 16 + 4 * s + e] = (uint8_t)(l4 >> (8 * la));
-  }
+  for (int t = NKC + tid; t < NM * 256; t += THREADS) limb_item(t);
   if (tid < kMRows) {
     s_Gs[tid] = 1.f / limb_scale(2.f * fmaxf(s_ws[4 * tid], s_ws[4 * tid + 2]));
     s_U[tid] = s_ws[4 * tid + 1] + s_ws[4 * tid + 3];
