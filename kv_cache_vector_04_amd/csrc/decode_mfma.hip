@@ -428,7 +428,7 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(MfmaDecodeArgs p) {
     }
   }
   __syncthreads();
-  constexpr int NBUF = 2;
+  constexpr int NBUF = 3;   // steps in flight per wave (measured: 2 and 4 slower)
   StepRegs<CBK, CBV> ring[NBUF] = {};
 #pragma unroll
   for (int k = 0; k < NBUF; ++k)
@@ -734,8 +734,8 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(MfmaDecodeArgs p) {
   // Software pipeline over a wave's steps: the key products of the next
   // step are issued beside the value sum of the current one (independent
   // work for the matrix cores and the vector ALU), then the next step's
-  // softmax runs.  Two register sets alternate (ring[0], ring[1]); a set is
-  // refilled two steps ahead once its value sum is issued.
+  // softmax runs.  NBUF register sets rotate (ring[0], ring[1], ...); a set
+  // is refilled NBUF steps ahead once its value sum is issued.
   {
     float w[4] = {0.f, 0.f, 0.f, 0.f};
     v4i cacc, qacc;
@@ -743,16 +743,16 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(MfmaDecodeArgs p) {
       keys(ring[0], cacc, qacc);
       scores(wave, ring[0], cacc, qacc, w);
     }
-    for (int gi = wave; gi < ng; gi += 2 * W) {
+    for (int gi = wave; gi < ng; gi += NBUF * W) {
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
+      for (int k = 0; k < NBUF; ++k) {
         const int gc = gi + k * W;
         if (gc < ng) {
           // next step's products (on stale registers past the end: unused)
-          keys(ring[k ^ 1], cacc, qacc);
+          keys(ring[(k + 1) % NBUF], cacc, qacc);
           values(ring[k], w);
-          if (gc + 2 * W < ng) load_step(gc + 2 * W, ring[k]);
-          if (gc + W < ng) scores(gc + W, ring[k ^ 1], cacc, qacc, w);
+          if (gc + NBUF * W < ng) load_step(gc + NBUF * W, ring[k]);
+          if (gc + W < ng) scores(gc + W, ring[(k + 1) % NBUF], cacc, qacc, w);
         }
       }
     }
