@@ -64,28 +64,6 @@ __device__ __forceinline__ float dppf(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
 }
 
-// v + v of the lane CTRL names, as one DPP-sourced add (every lane of the
-// row is a valid source for the rotations used here)
-template <int CTRL>
-__device__ __forceinline__ float dpp_add(float v) {
-  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, true));
-}
-
-// Combine each lane with lanes l ^ 32 and l ^ 16 (the four 16-lane rows).
-__device__ __forceinline__ float rows_max(float v) {
-  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-
-__device__ __forceinline__ float rows_sum(float v) {
-  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
 // Whole-wave reductions: DPP inside each 16-lane row (quad xor 1, quad
 // xor 2, half-row mirror, row mirror), then the four rows through scalar
 // reads; every lane gets the result.
@@ -193,7 +171,8 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(MfmaDecodeArgs p) {
   __shared__ __align__(16) float s_big[W * kMRows * (D + 2) > KP * kMRows * D
                                            ? W * kMRows * (D + 2) : KP * kMRows * D];
   __shared__ __align__(16) uint4 s_lb[NM][64]; // B operands: query limbs
-  __shared__ float s_F[kMRows], s_Gs[kMRows], s_T[kMRows], s_U[kMRows];
+  __shared__ float s_F[kMRows], s_T[kMRows], s_U[kMRows];
+  __shared__ float s_Fi[kMRows], s_Gi[kMRows];   // 1 / s_F and the QJL limb scale (powers of two)
   __shared__ float s_ws[16];                   // per-wave max |S q'| and sum
   __shared__ float s_vc[16];
   __shared__ float s_alpha[8];                 // key table in odd monomials
@@ -423,7 +402,9 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(MfmaDecodeArgs p) {
     tq += dppf<0x140>(tq);
     if (qj == 0) {
       // the inverse of a power of two (exact); the scan takes F = 1 / it
-      s_F[qr] = 1.f / limb_scale(2.f * p.alpha_max * mq);
+      const float fs = limb_scale(2.f * p.alpha_max * mq);
+      s_F[qr] = 1.f / fs;
+      s_Fi[qr] = fs;
       s_T[qr] = p.ktop * tq;
     }
   }
@@ -521,7 +502,7 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(MfmaDecodeArgs p) {
   __syncthreads();
   for (int t = NKC + tid; t < NM * 256; t += THREADS) limb_item(t);
   if (tid < kMRows) {
-    s_Gs[tid] = 1.f / limb_scale(2.f * fmaxf(s_ws[4 * tid], s_ws[4 * tid + 2]));
+    s_Gi[tid] = limb_scale(2.f * fmaxf(s_ws[4 * tid], s_ws[4 * tid + 2]));
     s_U[tid] = s_ws[4 * tid + 1] + s_ws[4 * tid + 3];
   }
   __syncthreads();
@@ -536,8 +517,8 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(MfmaDecodeArgs p) {
   float xw[kMRows], yw[kMRows], xc[kMRows], yc[kMRows];
 #pragma unroll
   for (int r = 0; r < kMRows; ++r) {
-    xw[r] = limb_w / s_F[r];
-    yw[r] = limb_w / s_Gs[r];
+    xw[r] = limb_w * s_Fi[r];     // exact: powers of two
+    yw[r] = limb_w * s_Gi[r];
     xc[r] = lg == 0 ? -s_T[r] : 0.f;
     yc[r] = lg == 0 ? -s_U[r] : 0.f;
   }
@@ -759,10 +740,27 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(MfmaDecodeArgs p) {
   }
 
   // ---- merge the lane rows, then the waves; write this range's record ----
+  // Reduce-scatter of the 32 accumulators (index f = 4 e + m) over the four
+  // 16-lane rows: each lane swap sums two accumulators across a pair of
+  // rows at once and keeps one of them per row, so 16-lane row G ends with
+  // the totals of query row m = 2 (G & 1) + G / 2, coordinates 8 lt + e.
+  float r1[16];
 #pragma unroll
-  for (int e = 0; e < 8; ++e)
+  for (int j = 0; j < 16; ++j) {
+    // lanes 0..31 keep f = 2 j, lanes 32..63 f = 2 j + 1
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[j >> 1][2 * (j & 1)]),
+                                                    __float_as_uint(acc[j >> 1][2 * (j & 1) + 1]), false, false);
+    r1[j] = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  }
+  float tot[8];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) acc[e][m] = rows_sum(acc[e][m]);
+  for (int e = 0; e < 8; ++e) {
+    // rows 0 and 2 keep r1[2 e], rows 1 and 3 r1[2 e + 1]
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(r1[2 * e]), __float_as_uint(r1[2 * e + 1]),
+                                                    false, false);
+    tot[e] = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+  }
+  const int mrow = 2 * ((lane >> 4) & 1) + (lane >> 5);
   // l_run: lane group g holds query row g's sums per token slot; sum the row
   l_run += dppf<0xB1>(l_run);
   l_run += dppf<0x4E>(l_run);
@@ -771,12 +769,8 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(MfmaDecodeArgs p) {
   __syncthreads();   // s_big (S q' partials) is free: wave merge space
   constexpr int REC = D + 2;
   float* mrg = s_big;   // [wave][row][D + 2]
-  if (lane < 16) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-#pragma unroll
-      for (int m = 0; m < 4; ++m) mrg[(wave * kMRows + m) * REC + 8 * lane + e] = acc[e][m];
-  }
+  for (int e = 0; e < 8; ++e) mrg[(wave * kMRows + mrow) * REC + 8 * lt + e] = tot[e];
   if (lt == 0) {
     mrg[(wave * kMRows + lg) * REC + D] = m_ref;
     mrg[(wave * kMRows + lg) * REC + D + 1] = l_run;
