@@ -409,11 +409,17 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(MfmaDecodeArgs p) {
     }
   }
   __syncthreads();
-  constexpr int NBUF = 3;   // steps in flight per wave (measured: 2 and 4 slower)
+  // steps in flight per wave (measured: 2 and 4 slower than 3; 4-bit key
+  // tables leave room for 2)
+  constexpr int NBUF = CBK == 4 ? 2 : 3;
   StepRegs<CBK, CBV> ring[NBUF] = {};
+  // A step past the wave's last one reloads that last step (cached; the
+  // data goes unused): every pass issues the same loads, so the wait before
+  // a step counts only the loads older than its own, not all in flight.
+  const int last_step = wave < ng ? wave + ((ng - 1 - wave) / W) * W : wave;
+  auto load_clamped = [&](int g, StepRegs<CBK, CBV>& R) { load_step(g < ng ? g : last_step, R); };
 #pragma unroll
-  for (int k = 0; k < NBUF; ++k)
-    if (wave + k * W < ng) load_step(wave + k * W, ring[k]);
+  for (int k = 0; k < NBUF; ++k) load_clamped(wave + k * W, ring[k]);
 
   // B operands: for product u, lane (g, n = 4 lam + r), dword s, byte e the
   // limb lam of (2 coef x 2^-j) / F_r, where the byte pairs with bit j of
@@ -720,21 +726,33 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(MfmaDecodeArgs p) {
   {
     float w[4] = {0.f, 0.f, 0.f, 0.f};
     v4i cacc, qacc;
-    if (wave < ng) {
+    // the wave's steps are wave, wave + W, ...: nst of them; step i sits in
+    // slot i % NBUF.  Whole rounds of NBUF steps first (every pass issues
+    // the same loads), then the rest.
+    const int nst = wave < ng ? (ng - 1 - wave) / W + 1 : 0;
+    if (nst > 0) {
       keys(ring[0], cacc, qacc);
       scores(wave, ring[0], cacc, qacc, w);
     }
-    for (int gi = wave; gi < ng; gi += NBUF * W) {
+    int it = 0;
+    for (; it + NBUF <= nst; it += NBUF) {
 #pragma unroll
       for (int k = 0; k < NBUF; ++k) {
-        const int gc = gi + k * W;
-        if (gc < ng) {
-          // next step's products (on stale registers past the end: unused)
-          keys(ring[(k + 1) % NBUF], cacc, qacc);
-          values(ring[k], w);
-          if (gc + NBUF * W < ng) load_step(gc + NBUF * W, ring[k]);
-          if (gc + W < ng) scores(gc + W, ring[(k + 1) % NBUF], cacc, qacc, w);
-        }
+        const int gc = wave + (it + k) * W;
+        // next step's products (on stale registers past the end: unused)
+        keys(ring[(k + 1) % NBUF], cacc, qacc);
+        values(ring[k], w);
+        load_clamped(gc + NBUF * W, ring[k]);
+        if (it + k + 1 < nst) scores(gc + W, ring[(k + 1) % NBUF], cacc, qacc, w);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < NBUF - 1; ++k) {
+      if (it + k < nst) {
+        const int gc = wave + (it + k) * W;
+        keys(ring[(k + 1) % NBUF], cacc, qacc);
+        values(ring[k], w);
+        if (it + k + 1 < nst) scores(gc + W, ring[(k + 1) % NBUF], cacc, qacc, w);
       }
     }
   }
