@@ -102,6 +102,19 @@ def test_attend_every_bit_width_pair(d, kb, vb, nq):
     _run(1, 4, 2, 130, nq, d, kb, vb, seed=1000 + 10 * kb + vb + d + 7 * nq)
 
 
+@pytest.mark.parametrize("kb", [4, 5])          # three and two code steps in flight per wave
+@pytest.mark.parametrize("steps", [3, 4, 5])     # code steps per wave
+def test_attend_load_ring_rounds(kb, steps):
+    """One KV head spread over every CU, each workgroup's range holding
+    8 x `steps` 16-token steps, so that each of its 8 waves runs `steps` of
+    them: whole rounds of the load ring with no tail, and tails of one and
+    two steps (the context follows the device's CU count)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    ctx = cus * 8 * 16 * steps
+    say("attend ring rounds: 4 q heads on 1 kv head, ctx %d (%d steps per wave), kb=%d" % (ctx, steps, kb))
+    _run(1, 4, 1, ctx, 1, 128, kb, 4, seed=500 + 10 * steps + kb)
+
+
 def test_attend_heavy_tails():
     say("attend Student-t(3) 8x2 heads ctx 5000")
     _run(1, 8, 2, 5000, 1, 128, 4, 4, seed=11, dist="t")
