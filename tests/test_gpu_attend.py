@@ -115,6 +115,30 @@ def test_attend_load_ring_rounds(kb, steps):
     _run(1, 4, 1, ctx, 1, 128, kb, 4, seed=500 + 10 * steps + kb)
 
 
+@pytest.mark.parametrize("d,nq", [(128, 1), (128, 3), (64, 1), (64, 4)])
+def test_attend_query_rope_few_rows(d, nq):
+    """RoPE on the queries in the few-row decode kernels (the matrix-core
+    kernel at d = 128, the vector-ALU kernel at d = 64): query a of every head
+    sits at position pos0 + a, here far enough out that the angle reduction
+    matters."""
+    B, Hq, Hkv, ctx, pos0 = 1, 8, 2, 1500, 4093
+    say("attend query RoPE d=%d nq=%d pos0=%d" % (d, nq, pos0))
+    rng = np.random.default_rng(40 + d + nq)
+    k = rng.standard_normal((B, Hkv, ctx, d)).astype(np.float16)
+    v = rng.standard_normal((B, Hkv, ctx, d)).astype(np.float16)
+    q = rng.standard_normal((B, Hq, nq, d)).astype(np.float16)
+    draws = synth.codec_draws(rng, d, m=d)
+    kc = tq.Codec(d, tq.TQ_PROD, 4, draws.flip, draws.S)
+    vc = tq.Codec(d, tq.TQ_MSE, 4, draws.flip)
+    kpk, vpk = tq.encode_kv(kc, vc, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda())
+    out, sc = tq.attend_decode(kc, vc, torch.from_numpy(q).cuda(), kpk, vpk, ctx, Hkv,
+                               rope=(10000.0, pos0), want_scores=True)
+    torch.cuda.synchronize()
+    ref_out, ref_sc = _oracle_attention(q, kpk, vpk, kc, vc, draws, B, Hkv, ctx,
+                                        q_rope_pos=pos0 + np.arange(nq))
+    print("scores", check_scores(to_np(sc), ref_sc), "| out", check_rows(to_np(out), ref_out))
+
+
 def test_attend_heavy_tails():
     say("attend Student-t(3) 8x2 heads ctx 5000")
     _run(1, 8, 2, 5000, 1, 128, 4, 4, seed=11, dist="t")
