@@ -24,7 +24,7 @@ def _codes_4d(pk, codec, B, Hkv, ctx):
     return {k: v.reshape((B, Hkv, ctx) + v.shape[1:]) for k, v in g.items()}
 
 
-def _oracle_attention(q, kpk, vpk, kc, vc, draws, B, Hkv, ctx, q_rope_pos=None):
+def _oracle_attention(q, kpk, vpk, kc, vc, draws, B, Hkv, ctx, q_rope_pos=None, scale=None):
     d = kc.d
     kcent, _ = oracle.codebook(d, kc.code_bits)
     vcent, _ = oracle.codebook(d, vc.code_bits)
@@ -34,7 +34,8 @@ def _oracle_attention(q, kpk, vpk, kc, vc, draws, B, Hkv, ctx, q_rope_pos=None):
     if q_rope_pos is not None:
         q64 = oracle.rope_interleaved(q64, q_rope_pos)
     return oracle.attention_from_codes(q64, _codes_4d(kpk, kc, B, Hkv, ctx),
-                                       _codes_4d(vpk, vc, B, Hkv, ctx), kb, vb, return_scores=True)
+                                       _codes_4d(vpk, vc, B, Hkv, ctx), kb, vb, scale=scale,
+                                       return_scores=True)
 
 
 def _run(B, Hq, Hkv, ctx, nq, d, kbits, vbits, seed, dist="normal"):
@@ -136,6 +137,28 @@ def test_attend_query_rope_few_rows(d, nq):
     torch.cuda.synchronize()
     ref_out, ref_sc = _oracle_attention(q, kpk, vpk, kc, vc, draws, B, Hkv, ctx,
                                         q_rope_pos=pos0 + np.arange(nq))
+    print("scores", check_scores(to_np(sc), ref_sc), "| out", check_rows(to_np(out), ref_out))
+
+
+@pytest.mark.parametrize("d,nq", [(128, 1), (64, 2), (64, 9), (128, 9)])
+def test_attend_fp32_queries_and_scale(d, nq):
+    """fp32 queries and an explicit softmax scale in every attention kernel:
+    the few-row decode kernels (G nq <= 16; d = 128 on the matrix cores, d = 64
+    on the vector ALU) and the many-query kernels at d = 64 and 128."""
+    B, Hq, Hkv, ctx, scale = 2, 4, 2, 700, 0.07
+    say("attend fp32 q, scale %g: d=%d nq=%d" % (scale, d, nq))
+    rng = np.random.default_rng(70 + d + nq)
+    k = rng.standard_normal((B, Hkv, ctx, d)).astype(np.float16)
+    v = rng.standard_normal((B, Hkv, ctx, d)).astype(np.float16)
+    q = rng.standard_normal((B, Hq, nq, d)).astype(np.float32)
+    draws = synth.codec_draws(rng, d, m=d)
+    kc = tq.Codec(d, tq.TQ_PROD, 3, draws.flip, draws.S)
+    vc = tq.Codec(d, tq.TQ_MSE, 3, draws.flip)
+    kpk, vpk = tq.encode_kv(kc, vc, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda())
+    out, sc = tq.attend_decode(kc, vc, torch.from_numpy(q).cuda(), kpk, vpk, ctx, Hkv, scale=scale,
+                               want_scores=True)
+    torch.cuda.synchronize()
+    ref_out, ref_sc = _oracle_attention(q, kpk, vpk, kc, vc, draws, B, Hkv, ctx, scale=scale)
     print("scores", check_scores(to_np(sc), ref_sc), "| out", check_rows(to_np(out), ref_out))
 
 
