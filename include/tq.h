@@ -318,7 +318,8 @@ int tq_decode_vq(const tq_vq_codec* c, const uint8_t* idx, const float* norm, in
  *   kc  TQ_PROD codec of the keys; vc TQ_MSE codec of the values; d = 64 or
  *       128 (other d: TQ_ERR_UNSUPPORTED)
  *   q   device [batch][hq][n_q][d] of `q_dtype`
- *   k,v host structs of device planes, rows [batch][hkv][ctx]
+ *   k,v host structs of device planes, rows [batch][hkv][ctx]; ctx < 2^25
+ *       (TQ_ERR_UNSUPPORTED beyond: 32-bit offsets inside a KV head)
  *   scale  0 selects 1/sqrt(d)
  *   out device [batch][hq][n_q][d] fp32
  *   scores_out  NULL, or device [batch][hq][n_q][ctx] fp32 receiving s_j

@@ -318,6 +318,9 @@ extern "C" int tq_attend_decode(const tq_codec* kc, const tq_codec* vc, const vo
   if (batch <= 0 || n_q <= 0 || hq <= 0 || hkv <= 0 || ctx <= 0) return TQ_ERR_INVALID_ARG;
   if (hq % hkv) return TQ_ERR_INVALID_ARG;
   if (hq / hkv > 16) return TQ_ERR_UNSUPPORTED;
+  // the kernels address one (batch, KV head)'s rows (up to 64 bytes each)
+  // with 32-bit byte offsets
+  if (ctx >= ((int64_t)1 << 25)) return TQ_ERR_UNSUPPORTED;
   if (!(scale >= 0.f)) return TQ_ERR_INVALID_ARG;
   if (q_rope != nullptr && (!(q_rope->base > 0.f) || q_rope->pos0 < 0)) return TQ_ERR_INVALID_ARG;
   if ((st = check_planes(kc, k)) != TQ_OK) return st;

@@ -341,6 +341,10 @@ def test_attend_and_scan_validation(L):
                ctypes.byref(pv), 32768, 0.0, fake, None, fake, need - 1, None) == tq.TQ_ERR_WORKSPACE
     assert att(ctypes.byref(kc), ctypes.byref(vc), fake, 0, 1, 1, 32, 8, None, ctypes.byref(pk),
                ctypes.byref(pv), 0, 0.0, fake, None, fake, need, None) == tq.TQ_ERR_INVALID_ARG
+    # contexts past the 32-bit row offsets inside a KV head
+    big = L.tq_attend_decode_workspace(1, 1, 32, 8, 1 << 25, 128)
+    assert att(ctypes.byref(kc), ctypes.byref(vc), fake, 0, 1, 1, 32, 8, None, ctypes.byref(pk),
+               ctypes.byref(pv), 1 << 25, 0.0, fake, None, fake, big, None) == tq.TQ_ERR_UNSUPPORTED
     ip = L.tq_inner_product
     assert ip(ctypes.byref(kc), fake, 1, 16, ctypes.byref(pk), 4096, None, 0, None, None, fake, 1 << 30,
               None) == tq.TQ_ERR_INVALID_ARG          # neither matrix nor top-k asked
