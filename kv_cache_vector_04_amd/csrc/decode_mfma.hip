@@ -91,6 +91,24 @@ __device__ __forceinline__ float wave_sum64(float v) {
   return (a + b) + (c + d);
 }
 
+// Maximum over the 16 lanes of each row: four maxima with a DPP-permuted
+// operand (quad xor 1, quad xor 2, half-row mirror, row mirror).  Written
+// out because fmaxf on a DPP move compiles to the move, the maximum and one
+// or two canonicalizing maxima per stage.  Two wait states before each DPP
+// read of a VGPR written by the previous VALU instruction.
+__device__ __forceinline__ float row16_max(float v) {
+  asm("s_nop 1\n\t"
+      "v_max_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_max_f32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_max_f32_dpp %0, %0, %0 row_mirror row_mask:0xf bank_mask:0xf"
+      : "+v"(v));
+  return v;
+}
+
 // The smallest power of two F with m / F <= 127 (1 for m = 0).
 __device__ __forceinline__ float limb_scale(float m) {
   if (!(m > 0.f)) return 1.f;
@@ -656,10 +674,7 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(MfmaDecodeArgs p) {
       p.scores_out[(row_base + lg) * p.ctx + tb + lt] = sv;
 
     // online softmax, lane group g = query row g
-    float mt = fmaxf(sv, dppf<0xB1>(sv));
-    mt = fmaxf(mt, dppf<0x4E>(mt));
-    mt = fmaxf(mt, dppf<0x141>(mt));
-    mt = fmaxf(mt, dppf<0x140>(mt));
+    const float mt = row16_max(sv);
     const bool bump = mt > m_ref + 8.f;
     if (__ballot(bump) != 0ull) {
       const float m_new = bump ? mt : m_ref;
@@ -700,8 +715,12 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(MfmaDecodeArgs p) {
       if constexpr (CBV == 4) {
         // the eight codes' byte offsets into the table: even codes from the
         // low nibbles, odd codes from the high nibbles, one byte each
-        const uint32_t ev = (bits & 0x0F0F0F0Fu) << 2;
-        const uint32_t od = (bits >> 2) & 0x3C3C3C3Cu;
+        uint32_t ev = (bits & 0x0F0F0F0Fu) << 2;
+        uint32_t od = (bits >> 2) & 0x3C3C3C3Cu;
+        // opaque to the optimizer, which would otherwise fold each byte
+        // extraction back into a shift and a mask of bits (two instructions
+        // per code instead of one)
+        asm("" : "+v"(ev), "+v"(od));
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const uint32_t off = __builtin_amdgcn_ubfe((e & 1) ? od : ev, 8 * (e >> 1), 8);
