@@ -758,6 +758,13 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(MfmaDecodeArgs p) {
 #pragma unroll
       for (int k = 0; k < NBUF; ++k) {
         const int gc = wave + (it + k) * W;
+        // Waves w and w + W / 2 share a SIMD, and the older one issues first
+        // whenever both can: left alone, it finishes its steps well before
+        // its partner, which then runs alone.  The younger wave takes the
+        // higher priority once a quarter of its steps are done (measured:
+        // 24.1 -> 23.6 us per GQA call, about 1 us less per Llama-shaped
+        // layer; from the first step, no gain).
+        if (wave >= W / 2 && it + k == nst / 4) __builtin_amdgcn_s_setprio(1);
         // next step's products (on stale registers past the end: unused)
         keys(ring[(k + 1) % NBUF], cacc, qacc);
         values(ring[k], w);
