@@ -294,14 +294,30 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(MfmaDecodeArgs p) {
   // Loads in the order they are needed, none waited on before the next one
   // is issued: the query rows (wave 0), the S rows of S q' (cached after the
   // first workgroups), and only once the query rows are rotated, the first
-  // NBUF steps' codes, which stay in flight during the rest of the set-up.
-  // (Issued at once, the codes of every workgroup would queue in front of
-  // the query rows.)  Each step refills its slot, NBUF steps ahead, once it
-  // is done with it.  Kernel arguments read at a per-lane index would be
-  // memory loads on this chain: the code tables reach LDS through scalar
-  // reads instead.
+  // steps' codes: one step after each of the first two set-up barriers and
+  // the rest once the set-up is done.  A CU holds a limited number of loads
+  // in flight, and while its waves' codes stream in at the CU's share of HBM
+  // bandwidth a wave that issues one more load waits at that instruction,
+  // and with it the set-up arithmetic behind it; spread out, the requests
+  // overlap the set-up without holding it back (measured: 24.1 -> 23.3 us
+  // per GQA call against all three steps requested after the rotation; all
+  // after the set-up, 24.0 us).  Issued before the rotation, the codes of
+  // every workgroup would queue in front of the query rows.  Each step
+  // refills its slot, NBUF steps ahead, once it is done with it.  Kernel
+  // arguments read at a per-lane index would be memory loads on this chain:
+  // the code tables reach LDS through scalar reads instead.
   // Wave 0 rotates all four query rows: lane (row r = lane / 16, j = lane % 16)
   // holds coordinates 8 j .. 8 j + 7 of row r.
+  // steps in flight per wave (measured: 2 and 4 slower than 3; 4-bit key
+  // tables leave room for 2)
+  constexpr int NBUF = CBK == 4 ? 2 : 3;
+  StepRegs<CBK, CBV> ring[NBUF] = {};
+  // A step past the wave's last one reloads that last step (cached; the
+  // data goes unused): every pass issues the same loads, so the wait before
+  // a step counts only the loads older than its own, not all in flight.
+  const int last_step = wave < ng ? wave + ((ng - 1 - wave) / W) * W : wave;
+  auto load_clamped = [&](int g, StepRegs<CBK, CBV>& R) { load_step(g < ng ? g : last_step, R); };
+
   const int qr = lane >> 4, qj = lane & 15;
   uint4 qraw0 = make_uint4(0u, 0u, 0u, 0u), qraw1 = qraw0;
   if (wave == 0 && qr < nrows) {
@@ -427,17 +443,7 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(MfmaDecodeArgs p) {
     }
   }
   __syncthreads();
-  // steps in flight per wave (measured: 2 and 4 slower than 3; 4-bit key
-  // tables leave room for 2)
-  constexpr int NBUF = CBK == 4 ? 2 : 3;
-  StepRegs<CBK, CBV> ring[NBUF] = {};
-  // A step past the wave's last one reloads that last step (cached; the
-  // data goes unused): every pass issues the same loads, so the wait before
-  // a step counts only the loads older than its own, not all in flight.
-  const int last_step = wave < ng ? wave + ((ng - 1 - wave) / W) * W : wave;
-  auto load_clamped = [&](int g, StepRegs<CBK, CBV>& R) { load_step(g < ng ? g : last_step, R); };
-#pragma unroll
-  for (int k = 0; k < NBUF; ++k) load_clamped(wave + k * W, ring[k]);
+  load_clamped(wave, ring[0]);
 
   // B operands: for product u, lane (g, n = 4 lam + r), dword s, byte e the
   // limb lam of (2 coef x 2^-j) / F_r, where the byte pairs with bit j of
@@ -508,6 +514,7 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(MfmaDecodeArgs p) {
     for (int r = 0; r < kMRows; ++r) s_big[(sp * kMRows + r) * D + si] = a[r];
   }
   __syncthreads();
+  load_clamped(wave + W, ring[1]);
   // S q' rows; each of waves 0..7 (two per row) also leaves its 64 values'
   // max |.| and sum, combined in a fixed order below
   if (tid < kMRows * D) {
@@ -530,6 +537,8 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(MfmaDecodeArgs p) {
     s_U[tid] = s_ws[4 * tid + 1] + s_ws[4 * tid + 3];
   }
   __syncthreads();
+#pragma unroll
+  for (int k = 2; k < NBUF; ++k) load_clamped(wave + k * W, ring[k]);
 
   uint4 bop[NM];
 #pragma unroll
