@@ -98,9 +98,9 @@ __global__ __launch_bounds__(kMqThreads, 2) void attend_mq_kernel(MqParams p) {
   __shared__ __align__(16) _Float16 s_sl[2][kMqTile][kMqStr];
   __shared__ __align__(16) _Float16 s_vh[2][D][kMqStr];
   __shared__ __align__(16) _Float16 s_vl[2][D][kMqStr];
-  __shared__ uint32_t s_kraw[2][kMqTile][KRW];
+  __shared__ uint32_t s_kraw[2][kMqTile][KRW + 1];   // a spare word per row: codes read two words
   __shared__ uint32_t s_sraw[2][kMqTile][2];
-  __shared__ uint32_t s_vraw[2][kMqTile][VRW];
+  __shared__ uint32_t s_vraw[2][kMqTile][VRW + 1];
   __shared__ float s_fk[2][kMqTile], s_fs[2][kMqTile], s_nv[2][kMqTile];
   __shared__ float s_kc[16], s_vc[16];
 
@@ -337,8 +337,8 @@ __global__ __launch_bounds__(kMqThreads, 2) void attend_mq_kernel(MqParams p) {
         for (int e = 0; e < 2; ++e) {
           const int bit = (c0 + j + e) * CBK;
           const int w = bit >> 5, sh = bit & 31;
-          uint32_t x = s_kraw[rb][tok][w] >> sh;
-          if (sh + CBK > 32) x |= s_kraw[rb][tok][w + 1] << (32 - sh);
+          // both words, joined by one funnel shift (no lane-dependent branch)
+          const uint32_t x = __builtin_amdgcn_alignbit(s_kraw[rb][tok][w + 1], s_kraw[rb][tok][w], sh);
           code[e] = x & ((1u << CBK) - 1u);
         }
         uint32_t h0, l0, h1, l1;
@@ -383,8 +383,7 @@ __global__ __launch_bounds__(kMqThreads, 2) void attend_mq_kernel(MqParams p) {
         for (int e = 0; e < 2; ++e) {
           const int col = col0 + j + e;
           const int tok = (col & ~12) | ((col & 4) << 1) | ((col & 8) >> 1);
-          uint32_t x = s_vraw[rb][tok][w] >> sh;
-          if (sh + CBV > 32) x |= s_vraw[rb][tok][w + 1] << (32 - sh);
+          const uint32_t x = __builtin_amdgcn_alignbit(s_vraw[rb][tok][w + 1], s_vraw[rb][tok][w], sh);
           val[e] = s_vc[x & ((1u << CBV) - 1u)] * s_nv[rb][tok];
         }
         uint32_t h0, l0, h1, l1;
