@@ -412,11 +412,12 @@ __global__ __launch_bounds__(kMqThreads, 2) void attend_mq_kernel(MqParams p) {
 
   int cur = 0;
   for (int64_t tile = 0; tile < p.ctx; tile += kMqTile, cur ^= 1) {
-    // the next tile's operands, beside this tile's products
-    if (tile + kMqTile < p.ctx) dequant(cur ^ 1);
-    // tile + 2 into the raw slot the previous dequantization freed, tile + 3 in flight
-    if (tile + 2 * kMqTile < p.ctx) store_raw(cur);
-    if (tile + 3 * kMqTile < p.ctx) load_raw(tile + 3 * kMqTile);
+    // the next tile's operands, beside this tile's products.  Unconditional,
+    // so that it shares a basic block with the score products and the
+    // compiler interleaves the two (measured 2164 -> 2113 us per ESM-2-shaped
+    // layer call); past the last tile it dequantizes stale raw words into the
+    // buffer that is not read again.
+    dequant(cur ^ 1);
     // ---- scores, transposed: rows = 32 tokens of block bk, column = query ----
     f32x16 S[2];
 #pragma unroll
@@ -507,6 +508,10 @@ __global__ __launch_bounds__(kMqThreads, 2) void attend_mq_kernel(MqParams p) {
         O[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(avl, bph, O[cb], 0, 0, 0);
       }
     }
+    // tile + 2 into the raw slot the previous dequantization freed (not read
+    // in this pass), tile + 3 in flight
+    if (tile + 2 * kMqTile < p.ctx) store_raw(cur);
+    if (tile + 3 * kMqTile < p.ctx) load_raw(tile + 3 * kMqTile);
     __syncthreads();     // buffer cur^1 written, buffer cur and raw slot cur^1 read
   }
 
