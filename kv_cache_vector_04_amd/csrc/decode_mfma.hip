@@ -712,37 +712,49 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(MfmaDecodeArgs p) {
     w[0] = w4.x; w[1] = w4.y; w[2] = w4.z; w[3] = w4.w;
   };
 
-  // value sum: rank-one updates of the accumulators with the weights w
+  // value sum: rank-one updates of the accumulators with the weights w.
+  // For 4-bit values each accumulator takes its four tokens' updates back to
+  // back (measured: 21.4 -> 21.1 us per GQA call against the token-major
+  // order, same bits); for 3-bit values the token-major order is 0.3 us
+  // faster per Llama-shaped call.
   auto values = [&](const StepRegs<CBK, CBV>& R, const float (&w)[4]) {
+    uint32_t bits[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      uint32_t bits;
       if constexpr (StepRegs<CBK, CBV>::VSTR)
-        bits = __builtin_amdgcn_alignbit(R.v1[i], R.v0[i], voff);
+        bits[i] = __builtin_amdgcn_alignbit(R.v1[i], R.v0[i], voff);
       else
-        bits = R.v0[i] >> voff;
-      if constexpr (CBV == 4) {
-        // the eight codes' byte offsets into the table: even codes from the
-        // low nibbles, odd codes from the high nibbles, one byte each
-        uint32_t ev = (bits & 0x0F0F0F0Fu) << 2;
-        uint32_t od = (bits >> 2) & 0x3C3C3C3Cu;
+        bits[i] = R.v0[i] >> voff;
+    }
+    if constexpr (CBV == 4) {
+      // the eight codes' byte offsets into the table: even codes from the
+      // low nibbles, odd codes from the high nibbles, one byte each
+      uint32_t ev[4], od[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ev[i] = (bits[i] & 0x0F0F0F0Fu) << 2;
+        od[i] = (bits[i] >> 2) & 0x3C3C3C3Cu;
         // opaque to the optimizer, which would otherwise fold each byte
         // extraction back into a shift and a mask of bits (two instructions
         // per code instead of one)
-        asm("" : "+v"(ev), "+v"(od));
+        asm("" : "+v"(ev[i]), "+v"(od[i]));
+      }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t off = __builtin_amdgcn_ubfe((e & 1) ? od : ev, 8 * (e >> 1), 8);
+      for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t off = __builtin_amdgcn_ubfe((e & 1) ? od[i] : ev[i], 8 * (e >> 1), 8);
           const float c = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(vc_lds) + off);
           acc[e] = __builtin_amdgcn_mfma_f32_4x4x1f32(w[i], c, acc[e], 0, 0, 0);
         }
-      } else {
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float c = vc_lds[(bits >> (CBV * e)) & ((1u << CBV) - 1u)];
+          const float c = vc_lds[(bits[i] >> (CBV * e)) & ((1u << CBV) - 1u)];
           acc[e] = __builtin_amdgcn_mfma_f32_4x4x1f32(w[i], c, acc[e], 0, 0, 0);
         }
-      }
     }
   };
 
